@@ -1,0 +1,309 @@
+"""Plain CPU definition of one batch-1 decoder-layer step (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
+this module. It shares no code with the GPU path.
+
+Page citations name the page title and section:
+
+* [P1] "RDNA4 Decode Kernel Fusion: Pipeline Barriers, Not Launches, Are the Win"
+* [P3] "backend-specific kernel fusion" (gearjunkie.de)
+* [P4] "Kernel fusion and block bridging" (jitllm docs)
+
+Readings taken where the pages are silent (each is listed in the design notes
+of the repository):
+
+* pre-norm residual layer: x += O(attn(norm(x))), then x += down(ffn(norm(x)));
+* RMSNorm: r = 1 / sqrt(mean(x^2) + eps), u = (x * r) * g, weight applied as
+  stored (not 1 + g);
+* RoPE: half-split pairs (i, i + d/2), angle p * theta^(-2i/d) formed in
+  float64, rotation by +angle;
+* attention scale 1/sqrt(d); query head h reads KV head floor(h / (n_q/n_kv));
+  the token is appended at position p first and attends to positions 0..p;
+* the cache stores rotated k and plain v rounded to the cache type; for a
+  bf16 cache the value is first rounded to fp32 (the GPU path's working
+  precision) and then to bf16, both round-to-nearest-even;
+* SwiGLU: h = silu(gate) * up with silu(z) = z / (1 + exp(-z));
+* 4-bit weights: w = scale * code, code a two's-complement nibble, element 2i
+  the low nibble of byte i, one fp16 scale per 32 consecutive inputs;
+* LM head: final RMSNorm, logits = W_head . x, argmax with the lowest index
+  winning ties.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ---------------------------------------------------------------- storage decode
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns to float64, exactly: a bf16 value is the upper half
+    of an IEEE binary32 with the lower 16 mantissa bits zero."""
+    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def q4_dequant(nib: np.ndarray, scales: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """4-bit block weights to real values: w[r, c] = scale[r, c // 32] * code[r, c].
+
+    ``nib`` is ``[rows, cols/2]`` bytes; element 2i is the low nibble of byte
+    i and element 2i+1 the high nibble; each nibble is a two's-complement
+    integer in [-8, 7]. ``scales`` is fp16 ``[rows, cols/32]``. The product of
+    an 11-bit significand and a 4-bit integer is exact in float32 and float64.
+    """
+    rows, half = nib.shape
+    cols = half * 2
+    lo = (nib & 0x0F).astype(np.int16)
+    hi = (nib >> 4).astype(np.int16)
+    lo[lo >= 8] -= 16
+    hi[hi >= 8] -= 16
+    codes = np.empty((rows, cols), dtype=np.int16)
+    codes[:, 0::2] = lo
+    codes[:, 1::2] = hi
+    s = scales.astype(np.float64)
+    w = codes.reshape(rows, cols // 32, 32).astype(np.float64) * s[:, :, None]
+    return w.reshape(rows, cols).astype(dtype)
+
+
+def dequant(st, dtype=np.float64) -> np.ndarray:
+    """A stored tensor (kind f32 / bf16 / q4) as real values of `dtype`."""
+    if st.kind == "f32":
+        return np.asarray(st.data, dtype=np.float32).astype(dtype)
+    if st.kind == "bf16":
+        return bf16_bits_to_f64(st.data).astype(dtype)
+    if st.kind == "q4":
+        return q4_dequant(st.data, st.scales, dtype)
+    raise ValueError(st.kind)
+
+
+# ---------------------------------------------------------------- layer steps
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm and its weight multiply ([P1] "Fusion removes the barrier by
+    removing the write": normalize the hidden state, then multiply by a
+    learned weight vector). m = mean(x^2); r = 1/sqrt(m + eps); u = (x r) g."""
+    m = np.mean(x * x)
+    r = 1.0 / np.sqrt(m + x.dtype.type(eps))
+    return (x * r) * g
+
+
+def gemv(w: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """A projection at batch 1: y = W u, W stored [out, in] ([P1] "Decode is
+    where the bubble has nowhere to go": QKV, output, gate/up and down
+    projections). No bias."""
+    return w @ u
+
+
+def rope_inv_freq(d: int, theta: float) -> np.ndarray:
+    """omega_i = theta^(-2i/d) for i in 0..d/2-1, in float64."""
+    i = np.arange(d // 2, dtype=np.float64)
+    return np.power(np.float64(theta), -2.0 * i / d)
+
+
+def rope(h: np.ndarray, p: int, theta: float) -> np.ndarray:
+    """RoPE on a set of heads ``h[n_heads, d]`` at position p ([P1] "Decode
+    is where the bubble has nowhere to go": RoPE on Q and K).
+
+    Pairs are (i, i + d/2). With phi = p * omega_i (float64),
+    h_i <- h_i cos(phi) - h_{i+d/2} sin(phi) and
+    h_{i+d/2} <- h_i sin(phi) + h_{i+d/2} cos(phi).
+    """
+    d = h.shape[-1]
+    phi = np.float64(p) * rope_inv_freq(d, theta)
+    c = np.cos(phi).astype(h.dtype)
+    s = np.sin(phi).astype(h.dtype)
+    a = h[..., : d // 2]
+    b = h[..., d // 2:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def round_to_cache(v: np.ndarray, kvtype: str) -> np.ndarray:
+    """The value the KV cache stores for `v` (append step; [P4] "Fusion":
+    k's rotation into its KV page and v's copy into its page).
+
+    fp32 cache: round to binary32 (nearest even). bf16 cache: round to
+    binary32, then keep the upper 16 bits rounded to nearest even, returned
+    as uint16 bit patterns.
+    """
+    f = np.asarray(v).astype(np.float32)
+    if kvtype == "f32":
+        return f
+    if kvtype != "bf16":
+        raise ValueError(kvtype)
+    bits = f.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> np.uint64(16)) & np.uint64(1)
+    out = (bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return out.astype(np.uint16)
+
+
+def cache_values(c: np.ndarray, kvtype: str, dtype) -> np.ndarray:
+    """Cache storage (fp32 values or bf16 bit patterns) as real values."""
+    if kvtype == "f32":
+        return c.astype(dtype)
+    return bf16_bits_to_f64(c).astype(dtype)
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, group: int) -> np.ndarray:
+    """Decode attention of one token against the cache ([P1] "Decode is where
+    the bubble has nowhere to go": attention against the KV cache).
+
+    ``q[n_q, d]``, ``K``/``V`` ``[n_kv, T, d]`` real values, T >= 1 positions.
+    For head h, j = h // group, s_t = (q_h . K_j[t]) / sqrt(d),
+    w_t = exp(s_t - max s), a_h = sum_t w_t V_j[t] / sum_t w_t.
+    """
+    n_q, d = q.shape
+    scale = q.dtype.type(1.0) / np.sqrt(q.dtype.type(d))
+    out = np.empty_like(q)
+    for h in range(n_q):
+        j = h // group
+        s = (K[j] @ q[h]) * scale
+        w = np.exp(s - s.max())
+        out[h] = (w @ V[j]) / w.sum()
+    return out
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z / (1 + exp(-z))."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """SwiGLU activation of the gated FFN ([P1] "Fusion removes the barrier
+    by removing the write": gate projection, up projection and SwiGLU):
+    h = silu(gate) * up."""
+    return silu(gate) * up
+
+
+# ---------------------------------------------------------------- the stack
+
+class Oracle:
+    """The decode stack on the CPU, one token at a time.
+
+    ``layers`` is a list of per-layer weight dicts in storage encoding
+    (keys attn_norm, wqkv, wo, ffn_norm, wgate, wup, wdown); ``glob`` holds
+    final_norm, head and embed. The cache is kept in its storage encoding
+    (fp32 values or bf16 bit patterns) as ``K[l][j, t, :]`` and ``V[l][j, t, :]``.
+    Weights are decoded to `dtype` when used (or once, with
+    ``keep_dequant=True``).
+    """
+
+    def __init__(self, cfg, layers, glob=None, dtype=np.float64, keep_dequant=None):
+        self.cfg = cfg
+        self.layers = layers
+        self.glob = glob
+        self.dtype = np.dtype(dtype).type
+        nbytes = sum(v.nbytes for lw in layers for v in lw.values())
+        self.keep = (nbytes < (1 << 30)) if keep_dequant is None else keep_dequant
+        self._deq = {}
+        cdt = np.float32 if cfg.kvtype == "f32" else np.uint16
+        shape = (cfg.n_kv_heads, cfg.max_ctx, cfg.head_dim)
+        self.K = [np.zeros(shape, dtype=cdt) for _ in layers]
+        self.V = [np.zeros(shape, dtype=cdt) for _ in layers]
+
+    # -- weights
+    def w(self, l: int, name: str) -> np.ndarray:
+        key = (l, name)
+        if key in self._deq:
+            return self._deq[key]
+        v = dequant(self.layers[l][name], self.dtype)
+        if self.keep:
+            self._deq[key] = v
+        return v
+
+    def gw(self, name: str) -> np.ndarray:
+        key = ("g", name)
+        if key in self._deq:
+            return self._deq[key]
+        v = dequant(self.glob[name], self.dtype)
+        if self.keep or name != "head":
+            self._deq[key] = v
+        return v
+
+    def load_prefill(self, l: int, K, V) -> None:
+        """Copy cache contents (storage encoding, ``[n_kv, n, d]``) into
+        positions 0..n-1 of layer l."""
+        n = K.data.shape[1]
+        self.K[l][:, :n] = K.data
+        self.V[l][:, :n] = V.data
+
+    # -- the layer's steps, in the order of [P1]
+    def qkv_rope_append(self, l: int, x: np.ndarray, p: int) -> np.ndarray:
+        """Input RMSNorm, QKV projection, RoPE on q and k, append k and v at p.
+        Returns q as ``[n_q, d]``."""
+        c = self.cfg
+        u = rmsnorm(x, self.w(l, "attn_norm"), c.rms_eps)
+        y = gemv(self.w(l, "wqkv"), u)
+        d = c.head_dim
+        q = y[: c.q_dim].reshape(c.n_q_heads, d)
+        k = y[c.q_dim: c.q_dim + c.kv_dim].reshape(c.n_kv_heads, d)
+        v = y[c.q_dim + c.kv_dim:].reshape(c.n_kv_heads, d)
+        q = rope(q, p, c.rope_theta)
+        k = rope(k, p, c.rope_theta)
+        self.K[l][:, p, :] = round_to_cache(k, c.kvtype)
+        self.V[l][:, p, :] = round_to_cache(v, c.kvtype)
+        return q
+
+    def attention(self, l: int, q: np.ndarray, p: int) -> np.ndarray:
+        """Attention of q over cache positions 0..p of layer l; returns the
+        head outputs concatenated in head order, ``[n_q * d]``."""
+        c = self.cfg
+        K = cache_values(self.K[l][:, : p + 1], c.kvtype, self.dtype)
+        V = cache_values(self.V[l][:, : p + 1], c.kvtype, self.dtype)
+        return attend(q, K, V, c.group).reshape(-1)
+
+    def ffn(self, l: int, x: np.ndarray) -> np.ndarray:
+        """Post-attention RMSNorm, gate and up projections, SwiGLU: h ``[F]``."""
+        u = rmsnorm(x, self.w(l, "ffn_norm"), self.cfg.rms_eps)
+        return swiglu(gemv(self.w(l, "wgate"), u), gemv(self.w(l, "wup"), u))
+
+    def layer(self, l: int, x: np.ndarray, p: int) -> np.ndarray:
+        """One decoder layer for the token at position p: returns the new x."""
+        q = self.qkv_rope_append(l, x, p)
+        a = self.attention(l, q, p)
+        x = x + gemv(self.w(l, "wo"), a)
+        h = self.ffn(l, x)
+        return x + gemv(self.w(l, "wdown"), h)
+
+    def embed(self, token: int) -> np.ndarray:
+        """x = E[token]: one row of the fp32 embedding table."""
+        st = self.glob["embed"]
+        return np.asarray(st.data[int(token)], dtype=np.float32).astype(self.dtype)
+
+    def step(self, token: int, p: int, layers=None) -> list:
+        """Decode one token at position p. Returns [x_in, x after layer 0,
+        x after layer 1, ...]."""
+        x = self.embed(token)
+        out = [x]
+        for l in (range(len(self.layers)) if layers is None else layers):
+            x = self.layer(l, x, p)
+            out.append(x)
+        return out
+
+    def logits(self, x: np.ndarray) -> np.ndarray:
+        xf = rmsnorm(x, self.gw("final_norm"), self.cfg.rms_eps)
+        return gemv(self.gw("head"), xf)
+
+    def greedy(self, x: np.ndarray) -> tuple:
+        """argmax of the logits (lowest index on ties) and the top-2 margin."""
+        z = self.logits(x)
+        i = int(np.argmax(z))
+        top2 = np.partition(z, -2)[-2:]
+        return i, float(top2[1] - top2[0])
+
+    # -- construction from the seeded recipe
+    @classmethod
+    def from_config(cls, cfg, n_layers=None, dtype=np.float64, with_globals=True,
+                    keep_dequant=None):
+        import synth
+        L = cfg.n_layers if n_layers is None else n_layers
+        layers = [synth.layer_weights(cfg, l) for l in range(L)]
+        glob = synth.model_globals(cfg) if with_globals else None
+        o = cls(cfg, layers, glob, dtype=dtype, keep_dequant=keep_dequant)
+        if not cfg.real_prefill and cfg.ctx > 0:
+            for l in range(L):
+                o.load_prefill(l, *synth.prefill(cfg, l))
+        return o
+
+    def prefill_by_decoding(self, toks) -> None:
+        """Fill positions 0..len(toks)-1 by decoding the tokens in order."""
+        for p, t in enumerate(toks):
+            self.step(int(t), p)
