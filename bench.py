@@ -1,0 +1,242 @@
+"""Batch-1 decode throughput of the fused layer stack on one MI355X.
+
+A step is one decode token through the whole stack: the embedding gather,
+every layer's five fused kernels (RMSNorm+QKV+RoPE+append, split-K
+attention, O projection + residual, RMSNorm+gate/up+SwiGLU, down projection
++ residual), and the position advance, replayed from one HIP graph. Inputs
+(weights, synthetic cache prefill, tokens) are seeded, synthetic and resident
+in HBM before timing starts.
+
+Reported (one JSON line): tok/s of the stack, the achieved HBM bandwidth of
+the token ((weight + KV bytes) per token x tok/s), a roofline entry for the
+dominant kernel (the gated FFN) timed per launch with HIP events on its
+launch stream, and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C4]
+                       [--unfused] [--eager] [--null-kernels] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def build_stack(cfg, flags, chunk):
+    import torch
+    import synth
+    from transformer_layer_amd.engine import DecodeStack
+
+    st = DecodeStack(cfg, flags=flags, attn_chunk=chunk)
+    t0 = time.time()
+    for l in range(cfg.n_layers):
+        st.set_layer(l, synth.layer_weights(cfg, l))
+        if cfg.ctx and not cfg.real_prefill:
+            st.set_prefill(l, *synth.prefill(cfg, l))
+        if l % 8 == 7:
+            log(f"uploaded {l + 1}/{cfg.n_layers} layers ({time.time() - t0:.0f}s)")
+    st.set_embedding(synth.embedding(cfg))
+    torch.cuda.synchronize()
+    return st
+
+
+def ffn_kernel_time(st, cfg, tokens_n: int):
+    """Average duration of the gated-FFN kernel over every layer of
+    `tokens_n` eager tokens, from HIP events recorded around each launch on
+    the stream the kernel runs on."""
+    import torch
+    from transformer_layer_amd import lib as L
+
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    evs = []
+    for _ in range(tokens_n):
+        st.embed_token(sp)
+        for l in range(cfg.n_layers):
+            w, s = st.wstruct[l], st.state[l]
+            L.dec_rmsnorm_gemv_qkv_rope(st.desc, w, s, sp)
+            L.dec_attn_splitk(st.desc, s, sp)
+            L.dec_gemv_residual(st.desc, w.wo, cfg.hidden, cfg.q_dim, s.attn, s.x, sp)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            L.dec_gated_ffn(st.desc, w.ffn_norm, w.wgate, w.wup, s.x, s.h, sp)
+            e1.record(stream)
+            evs.append((e0, e1))
+            L.dec_gemv_residual(st.desc, w.wdown, cfg.hidden, cfg.ffn, s.h, s.x, sp)
+        st.advance(cfg.ctx, cfg.ctx + cfg.steps, sp)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return float(np.mean(ms)) * 1e-3, len(ms)
+
+
+def cpu_baseline(cfg, budget_s: float = 15.0):
+    """The oracle (NumPy, float64) on a bounded sample: the first layers of
+    the same stack for one decode token at the first decode position, scaled
+    to tok/s of the whole stack."""
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    per_layer = []
+    n = 0
+    tok = int(synth.tokens(cfg)[0])
+    x = synth.embedding(cfg).data[tok].astype(np.float64)
+    t_all = time.time()
+    while n < cfg.n_layers:
+        o = oracle.Oracle(cfg, [synth.layer_weights(cfg, n)])
+        if cfg.ctx and not cfg.real_prefill:
+            o.load_prefill(0, *synth.prefill(cfg, n))
+        t0 = time.perf_counter()
+        x = o.layer(0, x, cfg.ctx)
+        per_layer.append(time.perf_counter() - t0)
+        n += 1
+        if sum(per_layer) >= budget_s or time.time() - t_all > 4 * budget_s:
+            break
+    t_layer = float(np.mean(per_layer))
+    tok_s = 1.0 / (t_layer * cfg.n_layers)
+    return {"value": tok_s, "unit": "tok/s", "cores": int(min(cores, blas_threads)) if blas_threads else cores,
+            "kind": "oracle",
+            "sample": f"layers 0..{n - 1} of the {cfg.n_layers}-layer stack, one decode token at position "
+                      f"{cfg.ctx} (float64 NumPy, weights decoded from their storage type at use); "
+                      f"{t_layer * 1e3:.0f} ms/layer scaled to the whole stack",
+            "host_cores_available": cores, "blas_threads": blas_threads}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--config", default="C4")
+    ap.add_argument("--unfused", action="store_true")
+    ap.add_argument("--eager", action="store_true")
+    ap.add_argument("--null-kernels", action="store_true")
+    ap.add_argument("--attn-chunk", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--ffn-tokens", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); "
+              "the multi-GPU sharding is a design note, not a runnable path", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    from transformer_layer_amd import lib as L
+
+    cfg = synth.CONFIGS[args.config]
+    flags = (L.DEC_UNFUSED if args.unfused else 0) | (L.DEC_NULL_KERNELS if args.null_kernels else 0)
+    log(f"config {cfg.name}: building stack ({cfg.n_layers} layers)")
+    st = build_stack(cfg, flags, args.attn_chunk)
+    toks = synth.tokens(cfg, cfg.steps)
+    st.set_token_list(toks)
+    lo, hi = cfg.ctx, cfg.ctx + cfg.steps
+
+    def reset():
+        st.set_pos(lo)
+        st.set_token(int(toks[0]))
+
+    reset()
+    stream = torch.cuda.current_stream()
+    if args.eager:
+        step = lambda: st.token_step(lo, hi)  # noqa: E731
+    else:
+        g = st.capture(lo, hi)
+        reset()
+        step = g.replay
+    log("warmup")
+    for _ in range(args.warmup):
+        step()
+    reset()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1)
+    err = st.check_err()
+    if err:
+        log(f"device error word {err:#x}")
+        return 1
+    tok_s = args.steps / (ms * 1e-3)
+    bpt = synth.token_bytes(cfg)
+    gbs = bpt * tok_s / 1e9
+    log(f"{tok_s:.1f} tok/s, {ms / args.steps:.3f} ms/token, {gbs:.0f} GB/s")
+
+    roof = None
+    if not args.null_kernels:
+        reset()
+        t_ffn, n_ffn = ffn_kernel_time(st, cfg, args.ffn_tokens)
+        ffn_bytes = synth.layer_weight_bytes(cfg)["ffn"]
+        ach = ffn_bytes / t_ffn / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "dec_gated_ffn (RMSNorm + gate/up GEMV + SwiGLU)",
+                "bytes_per_launch": int(ffn_bytes), "launches_timed": n_ffn,
+                "avg_launch_us": round(t_ffn * 1e6, 2)}
+        log(f"gated FFN: {t_ffn * 1e6:.1f} us/launch, {ach:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle sample)")
+        cpu = cpu_baseline(cfg)
+        log(f"oracle: {cpu['value']:.4f} tok/s")
+
+    out = {
+        "metric": "batch-1 decode tok/s + achieved HBM GB/s vs peak, 7B/9B-shaped stack",
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": cfg.n_layers, "hidden": cfg.hidden,
+                   "heads_q_kv": [cfg.n_q_heads, cfg.n_kv_heads], "head_dim": cfg.head_dim,
+                   "ffn": cfg.ffn, "weights": cfg.wtype, "kv_cache": cfg.kvtype,
+                   "context": cfg.ctx, "decode_window": cfg.steps, "batch": 1,
+                   "mode": ("unfused" if args.unfused else "fused") + ("-eager" if args.eager else "-graph")
+                           + ("-null" if args.null_kernels else ""),
+                   "kernels_per_layer": 10 if args.unfused else 5},
+        "bytes_per_token": int(bpt),
+        "hbm_gbs": round(gbs, 1),
+        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,218 @@
+/*
+ * dec_api.h - C ABI of libdec, a batch-1 decoder-layer engine for AMD MI355X
+ * (gfx950, wave64).
+ *
+ * One decode step of a pre-norm decoder layer, for a single token, follows
+ * the chain "RDNA4 Decode Kernel Fusion: Pipeline Barriers, Not Launches, Are
+ * the Win" lists in section "Decode is where the bubble has nowhere to go":
+ * input RMSNorm, QKV projection, RoPE on Q and K, attention against the KV
+ * cache, output projection, post-attention RMSNorm, gate and up projections,
+ * SwiGLU, down projection; the residual stream x is updated after the output
+ * projection and after the down projection. The same page's section "Fusion
+ * removes the barrier by removing the write" (and its opening questions)
+ * names the three fusions this library implements: RMSNorm and its weight
+ * multiply in the preamble of the following projection, RoPE folded into the
+ * QKV projection's epilogue, and gate, up and SwiGLU as one gated-FFN kernel
+ * whose wide intermediate never reaches memory. A fused layer is five
+ * kernels: dec_rmsnorm_gemv_qkv_rope, dec_attn_splitk, dec_gemv_residual
+ * (output projection), dec_gated_ffn, dec_gemv_residual (down projection).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, unless
+ *    stated otherwise. The library never allocates, frees or synchronizes,
+ *    and reads no device memory from the host; every call only enqueues
+ *    kernels on `stream` (a hipStream_t passed as void*; NULL is the null
+ *    stream), so every call may be captured into a HIP graph. The caller
+ *    keeps every buffer alive until the enqueued work has finished.
+ *  - Return value: DEC_OK (0), or a negative DEC_E_* code; nothing is
+ *    enqueued when the code is negative. dec_last_error() returns a
+ *    thread-local text for the last failure on the calling thread.
+ *  - Matrices are row-major [rows][cols]: y = W u means
+ *    y[r] = sum_c W[r][c] u[c]. Element types:
+ *      DEC_F32  float32
+ *      DEC_BF16 bfloat16 bit patterns (uint16)
+ *      DEC_Q4   4-bit blocks: `w` is [rows][cols/2] bytes, element 2i in the
+ *               low nibble of byte i and 2i+1 in the high nibble, each a
+ *               two's-complement code in [-8, 7]; `scales` is fp16
+ *               [rows][cols/32]; weight = scale[r][c/32] * code[r][c].
+ *    Each matrix base pointer is 16-byte aligned; cols is a multiple of 4
+ *    (f32), 8 (bf16) or 32 (q4), and at most 16384.
+ *  - Activations (x, q, attention output, h) are float32. Arithmetic is
+ *    float32 with float32 accumulation.
+ *  - The position of the token being decoded is a device int32 (`pos`), so a
+ *    captured graph replays unchanged from token to token. A position outside
+ *    [0, max_ctx) makes the kernels that read it set bit DEC_ERR_POS in the
+ *    device word `err` and store nothing.
+ */
+#ifndef DEC_API_H
+#define DEC_API_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DEC_ABI_VERSION 1
+
+enum dec_dtype { DEC_F32 = 0, DEC_BF16 = 1, DEC_Q4 = 2 };
+
+enum dec_status {
+  DEC_OK = 0,
+  DEC_E_NULL = -1,        /* a required pointer is NULL */
+  DEC_E_SHAPE = -2,       /* sizes violate the contract above */
+  DEC_E_DTYPE = -3,       /* unsupported element type for this argument */
+  DEC_E_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  DEC_E_LAUNCH = -5,      /* the HIP runtime rejected a launch */
+  DEC_E_UNSUPPORTED = -6  /* valid request this build does not implement */
+};
+
+/* bits of the device error word */
+#define DEC_ERR_POS 0x1u
+#define DEC_ERR_TOKEN 0x2u
+
+/* dec_layer_desc.flags */
+#define DEC_UNFUSED 0x1u       /* dec_layer_step runs the ten per-op kernels */
+#define DEC_NULL_KERNELS 0x2u  /* same launches, every kernel body returns at once */
+
+/* Static shape of one decoder layer (identical for every layer of a stack). */
+typedef struct {
+  int32_t hidden;      /* H */
+  int32_t n_q_heads;   /* query heads */
+  int32_t n_kv_heads;  /* key/value heads; n_q_heads % n_kv_heads == 0, ratio <= 8 */
+  int32_t head_dim;    /* d: 64 or 128 */
+  int32_t ffn;         /* F */
+  int32_t max_ctx;     /* cache positions per (layer, kv head) */
+  float rms_eps;       /* RMSNorm epsilon, added to mean(x^2) inside the root */
+  int32_t wtype;       /* projection weights: DEC_F32 | DEC_BF16 | DEC_Q4 */
+  int32_t ntype;       /* norm weights: DEC_F32 | DEC_BF16 */
+  int32_t kvtype;      /* KV cache: DEC_F32 | DEC_BF16 */
+  int32_t attn_chunk;  /* cache positions per attention split; 0 = library default */
+  uint32_t flags;      /* DEC_UNFUSED | DEC_NULL_KERNELS */
+} dec_layer_desc;
+
+/* A weight matrix: `w` the elements, `scales` the per-block fp16 scales
+   (DEC_Q4 only; NULL otherwise). */
+typedef struct {
+  const void* w;
+  const void* scales;
+} dec_mat;
+
+/* One layer's weights (all device memory, caller-owned).
+   attn_norm, ffn_norm: [H] in ntype.
+   wqkv: [(n_q + 2 n_kv) d][H]; rows are the q heads, then the k heads, then
+         the v heads, each head's d rows contiguous.
+   wo: [H][n_q d]. wgate, wup: [F][H]. wdown: [H][F]. */
+typedef struct {
+  const void* attn_norm;
+  dec_mat wqkv;
+  dec_mat wo;
+  const void* ffn_norm;
+  dec_mat wgate;
+  dec_mat wup;
+  dec_mat wdown;
+} dec_layer_weights;
+
+/* One layer's activations, cache and bookkeeping (device memory, caller-owned). */
+typedef struct {
+  float* x;            /* [H] residual stream, read and updated in place */
+  float* q;            /* [n_q d] rotated queries (written by the QKV kernel) */
+  float* attn;         /* [n_q d] attention output, heads in order */
+  float* h;            /* [F] SwiGLU output, input of the down projection */
+  float* part;         /* [dec_attn_part_floats(desc)] split partials */
+  uint32_t* counters;  /* [n_kv] arrival counters; zero before first use, and
+                          the attention kernel leaves them zero */
+  void* k_cache;       /* this layer's keys   [n_kv][max_ctx][d] in kvtype */
+  void* v_cache;       /* this layer's values [n_kv][max_ctx][d] in kvtype */
+  const int32_t* pos;  /* position p of the token being decoded */
+  const float* rope;   /* [max_ctx][d/2][2] (cos, sin) from dec_rope_table */
+  uint32_t* err;       /* device error word (bits are OR-ed in) */
+  float* scratch;      /* [dec_scratch_floats(desc)]; used by DEC_UNFUSED only,
+                          may be NULL otherwise */
+} dec_layer_state;
+
+/* ---- sizes of caller-provided buffers ---------------------------------- */
+
+/* floats needed by dec_layer_state.part for this shape (>= 1). */
+int64_t dec_attn_part_floats(const dec_layer_desc* desc);
+/* floats needed by dec_layer_state.scratch for the per-op path. */
+int64_t dec_scratch_floats(const dec_layer_desc* desc);
+
+/* ---- the five kernels of a fused layer -------------------------------- */
+
+/* Input RMSNorm + QKV projection + RoPE + KV-cache append, one kernel.
+   Passages: "RDNA4 Decode Kernel Fusion..." opening questions and section
+   "Fusion removes the barrier by removing the write" (RMSNorm and its multiply
+   in the projection's preamble; RoPE in the QKV projection's epilogue);
+   "Kernel fusion and block bridging", section "Fusion" (q's rotation, k's
+   rotation into its cache slot and v's copy into its slot in one launch).
+   Computes u = x / sqrt(mean(x^2) + eps) * attn_norm, y = Wqkv u, rotates
+   each q and k head by RoPE at position p (pairs (i, i + d/2), cos/sin from
+   the table), writes q (float32) and stores k, v rounded to kvtype
+   (nearest even) at cache position p of every kv head.
+   Reads: x, weights, rope, pos. Writes: q, k_cache[:, p], v_cache[:, p], err. */
+int dec_rmsnorm_gemv_qkv_rope(const dec_layer_desc* desc, const dec_layer_weights* w,
+                              const dec_layer_state* st, void* stream);
+
+/* Decode attention of the token's queries over cache positions 0..p,
+   split along the positions ("split-K"): each workgroup reduces one chunk of
+   one kv head for all of its query heads into (max, sum, unnormalized
+   output) partials, and the last workgroup of a kv head to arrive combines
+   them with a log-sum-exp rescale. Passage: "RDNA4 Decode Kernel Fusion...",
+   sections "Decode is where the bubble has nowhere to go" (attention against
+   the KV cache) and "Where fusion stops" (attention stays its own kernel).
+   Query head h uses kv head h / (n_q/n_kv); scores are scaled by 1/sqrt(d).
+   Reads: q, caches, pos. Writes: attn, part, counters (left zero), err. */
+int dec_attn_splitk(const dec_layer_desc* desc, const dec_layer_state* st, void* stream);
+
+/* x += W in: a projection fused with the residual add ("RDNA4 Decode Kernel
+   Fusion...", section "Decode is where the bubble has nowhere to go": output
+   projection and down projection). `w` is [rows][cols] in desc->wtype, `in`
+   is float32 [cols], `x` float32 [rows]. `in` and `x` must not overlap. */
+int dec_gemv_residual(const dec_layer_desc* desc, dec_mat w, int32_t rows, int32_t cols,
+                      const float* in, float* x, void* stream);
+
+/* Post-attention RMSNorm + gate and up projections + SwiGLU, one kernel
+   ("RDNA4 Decode Kernel Fusion...", section "Fusion removes the barrier by
+   removing the write": gate, up and SwiGLU collapse into one gated-FFN
+   kernel). u = x / sqrt(mean(x^2) + eps) * ffn_norm;
+   h[j] = silu(wgate[j] . u) * (wup[j] . u), silu(z) = z / (1 + exp(-z)).
+   The gate and up values stay in registers; only h (float32 [F]) is written. */
+int dec_gated_ffn(const dec_layer_desc* desc, const void* ffn_norm, dec_mat wgate, dec_mat wup,
+                  const float* x, float* h, void* stream);
+
+/* One whole decoder layer for the token at position *pos: the five kernels
+   above in order (or, with DEC_UNFUSED, the ten per-op kernels of the same
+   arithmetic: rmsnorm, weight multiply, QKV projection, RoPE + append,
+   attention, output projection + residual, rmsnorm with multiply, gate/up
+   projection, SwiGLU, down projection + residual). */
+int dec_layer_step(const dec_layer_desc* desc, const dec_layer_weights* w,
+                   const dec_layer_state* st, void* stream);
+
+/* ---- per-token bookkeeping --------------------------------------------- */
+
+/* RoPE table: table[p][i] = (cos(p w_i), sin(p w_i)), w_i = theta^(-2i/d),
+   for p < max_ctx and i < d/2; the angle and both functions are evaluated in
+   float64 on the device and rounded to float32. */
+int dec_rope_table(double theta, int32_t head_dim, int32_t max_ctx, float* table, void* stream);
+
+/* x = embed[*token] (float32 table [vocab][hidden]). A token outside
+   [0, vocab) sets bit DEC_ERR_TOKEN in err and writes zeros to x. */
+int dec_embed(const float* embed, int32_t vocab, int32_t hidden, const int32_t* token,
+              float* x, uint32_t* err, void* stream);
+
+/* Advance to the next token: p = *pos + 1, replaced by pos_lo when it falls
+   outside [pos_lo, pos_hi); *pos = p; if `tokens` is not NULL, *token = tokens[p - pos_lo]
+   (a teacher-forced list of pos_hi - pos_lo entries). One tiny kernel. */
+int dec_advance(int32_t* pos, int32_t pos_lo, int32_t pos_hi, const int32_t* tokens,
+                int32_t* token, void* stream);
+
+/* ---- misc --------------------------------------------------------------- */
+const char* dec_last_error(void);
+int dec_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DEC_API_H */

@@ -38,7 +38,7 @@ import numpy as np
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns to float64, exactly: a bf16 value is the upper half
     of an IEEE binary32 with the lower 16 mantissa bits zero."""
-    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64, copy=False)
 
 
 def q4_dequant(nib: np.ndarray, scales: np.ndarray, dtype=np.float64) -> np.ndarray:
@@ -51,16 +51,23 @@ def q4_dequant(nib: np.ndarray, scales: np.ndarray, dtype=np.float64) -> np.ndar
     """
     rows, half = nib.shape
     cols = half * 2
-    lo = (nib & 0x0F).astype(np.int16)
-    hi = (nib >> 4).astype(np.int16)
-    lo[lo >= 8] -= 16
-    hi[hi >= 8] -= 16
-    codes = np.empty((rows, cols), dtype=np.int16)
-    codes[:, 0::2] = lo
-    codes[:, 1::2] = hi
+    # two's-complement value of each 4-bit pattern 0..15
+    signed = np.array([0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5, -4, -3, -2, -1], dtype=np.float64)
+    codes = np.empty((rows, half, 2), dtype=np.float64)
+    codes[:, :, 0] = signed[nib & 0x0F]      # element 2i: low nibble of byte i
+    codes[:, :, 1] = signed[nib >> 4]        # element 2i+1: high nibble
     s = scales.astype(np.float64)
-    w = codes.reshape(rows, cols // 32, 32).astype(np.float64) * s[:, :, None]
-    return w.reshape(rows, cols).astype(dtype)
+    w = codes.reshape(rows, cols // 32, 32) * s[:, :, None]
+    return w.reshape(rows, cols).astype(dtype, copy=False)
+
+
+def dequant_rows(st, r0: int, r1: int, dtype=np.float64) -> np.ndarray:
+    """Rows r0..r1-1 of a stored matrix as real values of `dtype`."""
+    if st.kind == "q4":
+        return q4_dequant(st.data[r0:r1], st.scales[r0:r1], dtype)
+    if st.kind == "f32":
+        return np.asarray(st.data[r0:r1], dtype=np.float32).astype(dtype)
+    return bf16_bits_to_f64(st.data[r0:r1]).astype(dtype, copy=False)
 
 
 def dequant(st, dtype=np.float64) -> np.ndarray:
@@ -68,7 +75,7 @@ def dequant(st, dtype=np.float64) -> np.ndarray:
     if st.kind == "f32":
         return np.asarray(st.data, dtype=np.float32).astype(dtype)
     if st.kind == "bf16":
-        return bf16_bits_to_f64(st.data).astype(dtype)
+        return bf16_bits_to_f64(st.data).astype(dtype, copy=False)
     if st.kind == "q4":
         return q4_dequant(st.data, st.scales, dtype)
     raise ValueError(st.kind)
@@ -191,8 +198,8 @@ class Oracle:
         self.layers = layers
         self.glob = glob
         self.dtype = np.dtype(dtype).type
-        nbytes = sum(v.nbytes for lw in layers for v in lw.values())
-        self.keep = (nbytes < (1 << 30)) if keep_dequant is None else keep_dequant
+        n_elem = sum(int(np.prod(v.shape)) for lw in layers for v in lw.values())
+        self.keep = (n_elem * 8 <= (64 << 20)) if keep_dequant is None else keep_dequant
         self._deq = {}
         cdt = np.float32 if cfg.kvtype == "f32" else np.uint16
         shape = (cfg.n_kv_heads, cfg.max_ctx, cfg.head_dim)
@@ -200,6 +207,22 @@ class Oracle:
         self.V = [np.zeros(shape, dtype=cdt) for _ in layers]
 
     # -- weights
+    ROWS_PER_SLICE = 128
+
+    def proj(self, l: int, name: str, u: np.ndarray) -> np.ndarray:
+        """W u for layer l's matrix `name`. Without a decoded copy kept in
+        memory, the rows are decoded slice by slice (bounding memory); each
+        output is still one dot product over the whole row."""
+        if self.keep or (l, name) in self._deq:
+            return gemv(self.w(l, name), u)
+        st = self.layers[l][name]
+        rows = st.shape[0]
+        out = np.empty(rows, dtype=self.dtype)
+        for r0 in range(0, rows, self.ROWS_PER_SLICE):
+            r1 = min(rows, r0 + self.ROWS_PER_SLICE)
+            out[r0:r1] = gemv(dequant_rows(st, r0, r1, self.dtype), u)
+        return out
+
     def w(self, l: int, name: str) -> np.ndarray:
         key = (l, name)
         if key in self._deq:
@@ -231,7 +254,7 @@ class Oracle:
         Returns q as ``[n_q, d]``."""
         c = self.cfg
         u = rmsnorm(x, self.w(l, "attn_norm"), c.rms_eps)
-        y = gemv(self.w(l, "wqkv"), u)
+        y = self.proj(l, "wqkv", u)
         d = c.head_dim
         q = y[: c.q_dim].reshape(c.n_q_heads, d)
         k = y[c.q_dim: c.q_dim + c.kv_dim].reshape(c.n_kv_heads, d)
@@ -253,15 +276,15 @@ class Oracle:
     def ffn(self, l: int, x: np.ndarray) -> np.ndarray:
         """Post-attention RMSNorm, gate and up projections, SwiGLU: h ``[F]``."""
         u = rmsnorm(x, self.w(l, "ffn_norm"), self.cfg.rms_eps)
-        return swiglu(gemv(self.w(l, "wgate"), u), gemv(self.w(l, "wup"), u))
+        return swiglu(self.proj(l, "wgate", u), self.proj(l, "wup", u))
 
     def layer(self, l: int, x: np.ndarray, p: int) -> np.ndarray:
         """One decoder layer for the token at position p: returns the new x."""
         q = self.qkv_rope_append(l, x, p)
         a = self.attention(l, q, p)
-        x = x + gemv(self.w(l, "wo"), a)
+        x = x + self.proj(l, "wo", a)
         h = self.ffn(l, x)
-        return x + gemv(self.w(l, "wdown"), h)
+        return x + self.proj(l, "wdown", h)
 
     def embed(self, token: int) -> np.ndarray:
         """x = E[token]: one row of the fp32 embedding table."""

@@ -182,13 +182,18 @@ def prefill(cfg: DecodeConfig, layer: int) -> tuple:
     return tuple(out)
 
 
+def embedding(cfg: DecodeConfig) -> Stored:
+    """The fp32 token embedding table ``[vocab, H]``."""
+    return _normal_rows((cfg.seed, GLOBAL, EMBED), cfg.vocab, cfg.hidden, 1.0, 0.0, "f32")
+
+
 def model_globals(cfg: DecodeConfig) -> dict:
     """Final norm weight ``[H]``, LM head ``[vocab, H]`` and fp32 embedding ``[vocab, H]``."""
     s, H = cfg.seed, cfg.hidden
     return {
         "final_norm": _norm((s, GLOBAL, FINAL_NORM), H, cfg.ntype),
         "head": _normal_rows((s, GLOBAL, HEAD), cfg.vocab, H, 0.02, 0.0, cfg.htype),
-        "embed": _normal_rows((s, GLOBAL, EMBED), cfg.vocab, H, 1.0, 0.0, "f32"),
+        "embed": embedding(cfg),
     }
 
 

@@ -1,0 +1,213 @@
+"""Per-kernel parity: each fused kernel of the layer, called through the C
+ABI, against the CPU oracle's steps on the same seeded inputs.
+
+Shapes span several 16-byte granule tiles per lane with ragged tails (row
+lengths that are not a multiple of 64 granules), odd row counts, both
+column-split modes (one wave per row and four waves per row), every weight
+type, both cache types, head dims 64 and 128 and GQA groups 1..8.
+
+Tolerance: every kernel computes in float32 (exact bf16 / 4-bit weights,
+float32 inputs); a dot product of length n split over 64 lanes has a relative
+rounding error of order 2^-24 * sqrt(n); 1e-5 relative L2 bounds it with
+margin for n <= 16384. KV-cache bits are compared exactly, except where the
+oracle's exact value lies within that error of a bf16 rounding tie.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import check_rounded_slot, rel_l2
+from transformer_layer_amd import lib as L
+from transformer_layer_amd.engine import DecodeStack
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+SENT16 = 0x7FC1           # bf16 quiet-NaN pattern never produced by the kernels
+SENT32 = 0x7FC00001
+
+
+def _cfg(wtype, kvtype, H, nq, nkv, d, F=64, max_ctx=37, ntype=None):
+    return synth.tiny(hidden=H, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, ffn=F, wtype=wtype,
+                      ntype=ntype or ("f32" if wtype == "f32" else "bf16"), kvtype=kvtype,
+                      ctx=0, steps=max_ctx, seed=5)
+
+
+def _fill_sentinel(t):
+    if t.dtype == torch.int16:
+        t.fill_(SENT16)
+    else:
+        t.view(torch.int32).fill_(SENT32)
+
+
+QKV_CASES = [
+    # wtype, kvtype, H, n_q, n_kv, d
+    ("f32", "f32", 256, 4, 4, 64),
+    ("f32", "bf16", 1000, 2, 2, 64),      # ragged: 250 granules over 64 lanes
+    ("bf16", "bf16", 2176, 4, 2, 128),    # ragged: 272 granules
+    ("bf16", "bf16", 4096, 32, 8, 128),   # 9B-class layer shape
+    ("bf16", "bf16", 8192, 8, 1, 64),     # four waves per row
+    ("q4", "bf16", 2080, 8, 1, 64),       # 65 blocks per row
+    ("q4", "bf16", 4096, 32, 8, 128),
+]
+
+
+@pytest.mark.parametrize("wtype,kvtype,H,nq,nkv,d", QKV_CASES)
+def test_rmsnorm_gemv_qkv_rope(gpu, wtype, kvtype, H, nq, nkv, d):
+    cfg = _cfg(wtype, kvtype, H, nq, nkv, d)
+    p = 29
+    lw = synth.layer_weights(cfg, 0)
+    x = synth.rand_f32((5, 1, H), (H,))
+    st = DecodeStack(cfg, n_layers=1)
+    st.set_layer(0, lw)
+    _fill_sentinel(st.K)
+    _fill_sentinel(st.V)
+    st.x.copy_(torch.from_numpy(x))
+    st.set_pos(p)
+    L.dec_rmsnorm_gemv_qkv_rope(st.desc, st.wstruct[0], st.state[0])
+    torch.cuda.synchronize()
+    assert st.check_err() == 0
+
+    o = oracle.Oracle(cfg, [lw])
+    q_ora = o.qkv_rope_append(0, x.astype(np.float64), p)
+    # the oracle's exact (pre-rounding) k and v
+    u = oracle.rmsnorm(x.astype(np.float64), o.w(0, "attn_norm"), cfg.rms_eps)
+    y = oracle.gemv(o.w(0, "wqkv"), u)
+    k_ex = oracle.rope(y[cfg.q_dim: cfg.q_dim + cfg.kv_dim].reshape(nkv, d), p, cfg.rope_theta)
+    v_ex = y[cfg.q_dim + cfg.kv_dim:].reshape(nkv, d)
+
+    assert rel_l2(st.q.cpu().numpy(), q_ora.reshape(-1)) <= TOL
+    K = st.K[0].cpu().numpy()
+    V = st.V[0].cpu().numpy()
+    if kvtype == "bf16":
+        kg, vg = K[:, p].view(np.uint16), V[:, p].view(np.uint16)
+    else:
+        kg, vg = K[:, p], V[:, p]
+    check_rounded_slot(kg, o.K[0][:, p], k_ex, kvtype, TOL)
+    check_rounded_slot(vg, o.V[0][:, p], v_ex, kvtype, TOL)
+    # every other slot is untouched
+    sent = SENT16 if kvtype == "bf16" else SENT32
+    for C in (K, V):
+        bits = C.view(np.int16 if kvtype == "bf16" else np.int32)
+        mask = np.ones(bits.shape[1], dtype=bool)
+        mask[p] = False
+        assert np.all(bits[:, mask] == np.array(sent).astype(bits.dtype))
+
+
+GEMV_CASES = [
+    # wtype, rows, cols
+    ("f32", 777, 1000),
+    ("f32", 256, 1024),
+    ("bf16", 513, 2176),
+    ("bf16", 4096, 4096),
+    ("bf16", 1001, 11008),   # four waves per row, ragged
+    ("bf16", 4096, 12288),
+    ("q4", 999, 2080),
+    ("q4", 4096, 12288),     # four waves per row, 1.5 blocks per lane
+]
+
+
+@pytest.mark.parametrize("wtype,rows,cols", GEMV_CASES)
+def test_gemv_residual(gpu, wtype, rows, cols):
+    cfg = _cfg(wtype, "bf16", 256 if wtype != "q4" else 256, 4, 4, 64)
+    st = DecodeStack(cfg, n_layers=1)
+    W = synth.rand_matrix((6, rows, cols), rows, cols, wtype)
+    inp = synth.rand_f32((6, 2, cols), (cols,))
+    x0 = synth.rand_f32((6, 3, rows), (rows,))
+    from transformer_layer_amd.engine import _upload, _mat
+    dw = _upload(W, st.dev)
+    din = torch.from_numpy(inp).cuda()
+    dx = torch.from_numpy(x0).cuda()
+    L.dec_gemv_residual(st.desc, _mat(dw), rows, cols, din.data_ptr(), dx.data_ptr())
+    torch.cuda.synchronize()
+    ref = x0.astype(np.float64) + oracle.gemv(oracle.dequant(W), inp.astype(np.float64))
+    assert rel_l2(dx.cpu().numpy(), ref) <= TOL
+    # the residual-free part alone, so the check is not dominated by x0
+    delta = dx.cpu().numpy().astype(np.float64) - x0
+    assert rel_l2(delta, ref - x0) <= 4 * TOL
+
+
+FFN_CASES = [
+    ("f32", 256, 1024),
+    ("bf16", 2176, 1000),
+    ("bf16", 4096, 12288),
+    ("bf16", 8192, 640),
+    ("q4", 4096, 12288),
+    ("q4", 2080, 352),
+]
+
+
+@pytest.mark.parametrize("wtype,H,F", FFN_CASES)
+def test_gated_ffn(gpu, wtype, H, F):
+    cfg = _cfg(wtype, "bf16", H, 4, 4, 64, F=F)
+    st = DecodeStack(cfg, n_layers=1)
+    g = synth.rand_norm((7, 1, H), H, cfg.ntype)
+    Wg = synth.rand_matrix((7, 2, F), F, H, wtype)
+    Wu = synth.rand_matrix((7, 3, F), F, H, wtype)
+    x = synth.rand_f32((7, 4, H), (H,))
+    from transformer_layer_amd.engine import _upload, _mat
+    dg, dwg, dwu = _upload(g, st.dev), _upload(Wg, st.dev), _upload(Wu, st.dev)
+    dx = torch.from_numpy(x).cuda()
+    dh = torch.zeros(F, dtype=torch.float32, device="cuda")
+    L.dec_gated_ffn(st.desc, dg[0].data_ptr(), _mat(dwg), _mat(dwu), dx.data_ptr(), dh.data_ptr())
+    torch.cuda.synchronize()
+    u = oracle.rmsnorm(x.astype(np.float64), oracle.dequant(g), cfg.rms_eps)
+    ref = oracle.swiglu(oracle.gemv(oracle.dequant(Wg), u), oracle.gemv(oracle.dequant(Wu), u))
+    assert rel_l2(dh.cpu().numpy(), ref) <= TOL
+
+
+ATTN_CASES = [
+    # d, kvtype, n_q, n_kv, max_ctx, positions, chunk
+    (64, "f32", 4, 4, 24, (0, 15, 23), 0),
+    (64, "bf16", 32, 8, 640, (0, 511, 600, 639), 0),
+    (128, "bf16", 32, 32, 2176, (2047, 2100), 0),
+    (128, "bf16", 32, 8, 4352, (4095, 4351), 0),
+    (128, "bf16", 32, 8, 8448, (8191, 8447), 0),
+    (128, "bf16", 16, 2, 300, (0, 1, 16, 17, 299), 16),   # one-row and ragged splits
+    (128, "f32", 8, 1, 100, (99, 50), 48),
+    (64, "bf16", 8, 4, 200, (199,), 256),                 # a single split
+]
+
+
+@pytest.mark.parametrize("d,kvtype,nq,nkv,max_ctx,positions,chunk", ATTN_CASES)
+def test_attn_splitk(gpu, d, kvtype, nq, nkv, max_ctx, positions, chunk):
+    H = 256
+    cfg = synth.tiny(hidden=H, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, ffn=256, wtype="bf16",
+                     ntype="bf16", kvtype=kvtype, ctx=0, steps=max_ctx, seed=8)
+    st = DecodeStack(cfg, n_layers=1, attn_chunk=chunk)
+    std = 0.02 * np.sqrt(4096)
+    K = synth.rand_cache((8, 1, max_ctx), nkv, max_ctx, d, kvtype, std)
+    V = synth.rand_cache((8, 2, max_ctx), nkv, max_ctx, d, kvtype, std)
+    st.set_prefill(0, K, V)
+    Kv = oracle.ref.cache_values(K.data, kvtype, np.float64)
+    Vv = oracle.ref.cache_values(V.data, kvtype, np.float64)
+    for i, p in enumerate(positions):
+        q = synth.rand_f32((8, 3, i), (nq, d), std=std)
+        st.q.copy_(torch.from_numpy(q.reshape(-1)))
+        st.set_pos(p)
+        L.dec_attn_splitk(st.desc, st.state[0])
+        torch.cuda.synchronize()
+        ref = oracle.attend(q.astype(np.float64), Kv[:, : p + 1], Vv[:, : p + 1], nq // nkv)
+        assert rel_l2(st.attn.cpu().numpy(), ref.reshape(-1)) <= TOL, f"pos {p}"
+        assert int(st.counters.abs().sum().item()) == 0, "arrival counters not reset"
+    assert st.check_err() == 0
+
+
+def test_position_out_of_range_sets_error_and_stores_nothing(gpu):
+    cfg = _cfg("bf16", "bf16", 256, 4, 4, 64, max_ctx=8)
+    lw = synth.layer_weights(cfg, 0)
+    st = DecodeStack(cfg, n_layers=1)
+    st.set_layer(0, lw)
+    _fill_sentinel(st.K)
+    _fill_sentinel(st.V)
+    st.q.fill_(7.0)
+    for bad in (8, -1, 1000):
+        st.err.zero_()
+        st.set_pos(bad)
+        L.dec_rmsnorm_gemv_qkv_rope(st.desc, st.wstruct[0], st.state[0])
+        L.dec_attn_splitk(st.desc, st.state[0])
+        torch.cuda.synchronize()
+        assert st.check_err() & L.DEC_ERR_POS
+    assert bool(torch.all(st.K == SENT16)) and bool(torch.all(st.V == SENT16))
+    assert bool(torch.all(st.q == 7.0))

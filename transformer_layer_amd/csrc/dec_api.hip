@@ -1,0 +1,329 @@
+// C ABI of libdec: argument checks, launch planning, error reporting.
+// Every entry point validates on the host, then only enqueues kernels on the
+// caller's stream: no allocation, no synchronization, no device reads.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dec_api.h"
+#include "dec_internal.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DEC_E_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return DEC_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ge_of(int wtype) { return wtype == DEC_F32 ? 4 : wtype == DEC_BF16 ? 8 : 32; }
+
+int check_desc(const dec_layer_desc* d) {
+  if (!d) return fail(DEC_E_NULL, "desc is NULL");
+  if (d->wtype < DEC_F32 || d->wtype > DEC_Q4) return fail(DEC_E_DTYPE, "wtype %d", d->wtype);
+  if (d->ntype != DEC_F32 && d->ntype != DEC_BF16) return fail(DEC_E_DTYPE, "ntype %d", d->ntype);
+  if (d->kvtype != DEC_F32 && d->kvtype != DEC_BF16) return fail(DEC_E_DTYPE, "kvtype %d", d->kvtype);
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(DEC_E_SHAPE, "head_dim %d (64 or 128)", d->head_dim);
+  if (d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->n_q_heads % d->n_kv_heads)
+    return fail(DEC_E_SHAPE, "heads %d/%d", d->n_q_heads, d->n_kv_heads);
+  const int g = d->n_q_heads / d->n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return fail(DEC_E_SHAPE, "group %d (1, 2, 4 or 8)", g);
+  const int ge = ge_of(d->wtype);
+  const int qd = d->n_q_heads * d->head_dim;
+  for (int c : {d->hidden, d->ffn, qd})
+    if (c <= 0 || c % ge || c > 16384) return fail(DEC_E_SHAPE, "length %d (multiple of %d, <= 16384)", c, ge);
+  if (d->max_ctx <= 0 || d->max_ctx > (1 << 20)) return fail(DEC_E_SHAPE, "max_ctx %d", d->max_ctx);
+  if (!(d->rms_eps >= 0.0f)) return fail(DEC_E_SHAPE, "rms_eps");
+  if (d->attn_chunk < 0 || d->attn_chunk > 256) return fail(DEC_E_SHAPE, "attn_chunk %d (0..256)", d->attn_chunk);
+  int chunk, ns;
+  dec::attn_plan(d->n_kv_heads, d->max_ctx, d->attn_chunk, &chunk, &ns);
+  if (ns > 256) return fail(DEC_E_SHAPE, "max_ctx %d needs %d splits (max 256)", d->max_ctx, ns);
+  return DEC_OK;
+}
+
+int check_mat(const dec_layer_desc* d, dec_mat m, const char* name) {
+  if (!m.w) return fail(DEC_E_NULL, "%s is NULL", name);
+  if (!aligned16(m.w)) return fail(DEC_E_ALIGN, "%s not 16-byte aligned", name);
+  if (d->wtype == DEC_Q4 && !m.scales) return fail(DEC_E_NULL, "%s scales are NULL", name);
+  return DEC_OK;
+}
+
+hipError_t gemv(int wtype, int epi, const dec::GemvArgs& a, hipStream_t s) {
+  switch (wtype) {
+    case DEC_F32: return dec::launch_gemv_f32(epi, a, s);
+    case DEC_BF16: return dec::launch_gemv_bf16(epi, a, s);
+    default: return dec::launch_gemv_q4(epi, a, s);
+  }
+}
+
+dec::GemvArgs base_args(const dec_layer_desc* d) {
+  dec::GemvArgs a;
+  memset(&a, 0, sizeof a);
+  a.ntype = d->ntype == DEC_BF16 ? 1 : 0;
+  a.eps = d->rms_eps;
+  a.nq = d->n_q_heads;
+  a.nkv = d->n_kv_heads;
+  a.d = d->head_dim;
+  a.max_ctx = d->max_ctx;
+  a.kvtype = d->kvtype == DEC_BF16 ? 1 : 0;
+  a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
+  return a;
+}
+
+int qkv_launch(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st,
+               hipStream_t s) {
+  dec::GemvArgs a = base_args(d);
+  a.W = w->wqkv.w;
+  a.S = w->wqkv.scales;
+  a.rows = (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+  a.cols = d->hidden;
+  a.ntask = a.rows / 2;
+  a.in = st->x;
+  a.norm = w->attn_norm;
+  a.y = st->q;
+  a.pos = st->pos;
+  a.rope = st->rope;
+  a.kc = st->k_cache;
+  a.vc = st->v_cache;
+  a.err = st->err;
+  return launched(gemv(d->wtype, dec::kEpiQkv, a, s), "rmsnorm_gemv_qkv_rope");
+}
+
+int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t s) {
+  dec::AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = st->q;
+  a.kc = st->k_cache;
+  a.vc = st->v_cache;
+  a.part = st->part;
+  a.counters = st->counters;
+  a.out = st->attn;
+  a.pos = st->pos;
+  a.err = st->err;
+  a.nq = d->n_q_heads;
+  a.nkv = d->n_kv_heads;
+  a.d = d->head_dim;
+  a.max_ctx = d->max_ctx;
+  a.kvtype = d->kvtype == DEC_BF16 ? 1 : 0;
+  a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
+  dec::attn_plan(d->n_kv_heads, d->max_ctx, d->attn_chunk, &a.chunk, &a.nsplit);
+  return launched(dec::launch_attn(a, s), "attn_splitk");
+}
+
+int residual_launch(const dec_layer_desc* d, dec_mat w, int rows, int cols, const float* in,
+                    float* x, hipStream_t s) {
+  dec::GemvArgs a = base_args(d);
+  a.W = w.w;
+  a.S = w.scales;
+  a.rows = rows;
+  a.cols = cols;
+  a.ntask = (rows + 1) / 2;
+  a.in = in;
+  a.x = x;
+  return launched(gemv(d->wtype, dec::kEpiResidual, a, s), "gemv_residual");
+}
+
+int ffn_launch(const dec_layer_desc* d, const void* norm, dec_mat wg, dec_mat wu, const float* x,
+               float* h, hipStream_t s) {
+  dec::GemvArgs a = base_args(d);
+  a.W = wg.w;
+  a.S = wg.scales;
+  a.W2 = wu.w;
+  a.S2 = wu.scales;
+  a.rows = d->ffn;
+  a.cols = d->hidden;
+  a.ntask = d->ffn;
+  a.in = x;
+  a.norm = norm;
+  a.y = h;
+  return launched(gemv(d->wtype, dec::kEpiSwiglu, a, s), "gated_ffn");
+}
+
+int check_state(const dec_layer_state* st, bool scratch) {
+  if (!st) return fail(DEC_E_NULL, "state is NULL");
+  if (!st->x || !st->q || !st->attn || !st->h || !st->part || !st->counters || !st->k_cache ||
+      !st->v_cache || !st->pos || !st->rope || !st->err)
+    return fail(DEC_E_NULL, "a state pointer is NULL");
+  if (scratch && !st->scratch) return fail(DEC_E_NULL, "scratch is NULL (needed by DEC_UNFUSED)");
+  for (const void* p : {(const void*)st->x, (const void*)st->q, (const void*)st->attn,
+                        (const void*)st->h, (const void*)st->k_cache, (const void*)st->v_cache})
+    if (!aligned16(p)) return fail(DEC_E_ALIGN, "state buffer not 16-byte aligned");
+  if (scratch && !aligned16(st->scratch)) return fail(DEC_E_ALIGN, "scratch not 16-byte aligned");
+  return DEC_OK;
+}
+
+int check_weights(const dec_layer_desc* d, const dec_layer_weights* w) {
+  if (!w) return fail(DEC_E_NULL, "weights are NULL");
+  if (!w->attn_norm || !w->ffn_norm) return fail(DEC_E_NULL, "norm weight is NULL");
+  int rc;
+  if ((rc = check_mat(d, w->wqkv, "wqkv")) || (rc = check_mat(d, w->wo, "wo")) ||
+      (rc = check_mat(d, w->wgate, "wgate")) || (rc = check_mat(d, w->wup, "wup")) ||
+      (rc = check_mat(d, w->wdown, "wdown")))
+    return rc;
+  return DEC_OK;
+}
+
+int64_t pad4(int64_t n) { return (n + 3) / 4 * 4; }
+
+}  // namespace
+
+extern "C" {
+
+int dec_abi_version(void) { return DEC_ABI_VERSION; }
+
+const char* dec_last_error(void) { return g_err; }
+
+int64_t dec_attn_part_floats(const dec_layer_desc* d) {
+  if (check_desc(d)) return -1;
+  int chunk, ns;
+  dec::attn_plan(d->n_kv_heads, d->max_ctx, d->attn_chunk, &chunk, &ns);
+  return int64_t(d->n_q_heads) * ns * (d->head_dim + 2);
+}
+
+int64_t dec_scratch_floats(const dec_layer_desc* d) {
+  if (check_desc(d)) return -1;
+  const int64_t nqkv = int64_t(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+  return pad4(d->hidden) + pad4(nqkv) + 2 * pad4(d->ffn);
+}
+
+int dec_rmsnorm_gemv_qkv_rope(const dec_layer_desc* d, const dec_layer_weights* w,
+                              const dec_layer_state* st, void* stream) {
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_state(st, false))) return rc;
+  if (!w) return fail(DEC_E_NULL, "weights are NULL");
+  if (!w->attn_norm) return fail(DEC_E_NULL, "attn_norm is NULL");
+  if ((rc = check_mat(d, w->wqkv, "wqkv"))) return rc;
+  return qkv_launch(d, w, st, hipStream_t(stream));
+}
+
+int dec_attn_splitk(const dec_layer_desc* d, const dec_layer_state* st, void* stream) {
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_state(st, false))) return rc;
+  return attn_launch(d, st, hipStream_t(stream));
+}
+
+int dec_gemv_residual(const dec_layer_desc* d, dec_mat w, int32_t rows, int32_t cols,
+                      const float* in, float* x, void* stream) {
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_mat(d, w, "w"))) return rc;
+  if (!in || !x) return fail(DEC_E_NULL, "in/x is NULL");
+  if (!aligned16(in)) return fail(DEC_E_ALIGN, "in not 16-byte aligned");
+  const int ge = ge_of(d->wtype);
+  if (rows <= 0 || cols <= 0 || cols % ge || cols > 16384)
+    return fail(DEC_E_SHAPE, "rows %d cols %d (cols a multiple of %d, <= 16384)", rows, cols, ge);
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* ib = reinterpret_cast<const char*>(in);
+  if (xb < ib + size_t(cols) * 4 && ib < xb + size_t(rows) * 4) return fail(DEC_E_SHAPE, "in and x overlap");
+  return residual_launch(d, w, rows, cols, in, x, hipStream_t(stream));
+}
+
+int dec_gated_ffn(const dec_layer_desc* d, const void* ffn_norm, dec_mat wgate, dec_mat wup,
+                  const float* x, float* h, void* stream) {
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_mat(d, wgate, "wgate")) || (rc = check_mat(d, wup, "wup")))
+    return rc;
+  if (!ffn_norm || !x || !h) return fail(DEC_E_NULL, "ffn_norm/x/h is NULL");
+  if (!aligned16(x)) return fail(DEC_E_ALIGN, "x not 16-byte aligned");
+  return ffn_launch(d, ffn_norm, wgate, wup, x, h, hipStream_t(stream));
+}
+
+int dec_layer_step(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st,
+                   void* stream) {
+  int rc;
+  const bool unfused = d && (d->flags & DEC_UNFUSED);
+  if ((rc = check_desc(d)) || (rc = check_weights(d, w)) || (rc = check_state(st, unfused))) return rc;
+  hipStream_t s = hipStream_t(stream);
+  const int H = d->hidden, F = d->ffn, qd = d->n_q_heads * d->head_dim;
+  if (!unfused) {
+    if ((rc = qkv_launch(d, w, st, s))) return rc;
+    if ((rc = attn_launch(d, st, s))) return rc;
+    if ((rc = residual_launch(d, w->wo, H, qd, st->attn, st->x, s))) return rc;
+    if ((rc = ffn_launch(d, w->ffn_norm, w->wgate, w->wup, st->x, st->h, s))) return rc;
+    return residual_launch(d, w->wdown, H, F, st->h, st->x, s);
+  }
+  // The ten per-op kernels of the same arithmetic: rmsnorm, weight multiply,
+  // QKV projection, RoPE + append, attention, output projection + residual,
+  // rmsnorm with multiply, gate/up projection, SwiGLU, down projection +
+  // residual. Intermediates go through `scratch`.
+  const int nullk = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
+  const int ntype = d->ntype == DEC_BF16 ? 1 : 0;
+  const int nqkv = (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+  float* u = st->scratch;
+  float* y = u + pad4(H);
+  float* gate = y + pad4(nqkv);
+  float* up = gate + pad4(F);
+  if ((rc = launched(dec::launch_rmsnorm_like(st->x, nullptr, ntype, u, H, d->rms_eps, d->wtype, 0, nullk, s),
+                     "rmsnorm")))
+    return rc;
+  if ((rc = launched(dec::launch_mul(u, w->attn_norm, ntype, H, nullk, s), "mul"))) return rc;
+  dec::GemvArgs a = base_args(d);
+  a.W = w->wqkv.w;
+  a.S = w->wqkv.scales;
+  a.rows = nqkv;
+  a.cols = H;
+  a.ntask = (nqkv + 1) / 2;
+  a.in = u;
+  a.y = y;
+  if ((rc = launched(gemv(d->wtype, dec::kEpiStore, a, s), "gemv_qkv"))) return rc;
+  if ((rc = launched(dec::launch_rope_append(y, st->q, st->k_cache, st->v_cache, st->pos, st->rope, st->err,
+                                             d->n_q_heads, d->n_kv_heads, d->head_dim, d->max_ctx,
+                                             d->kvtype == DEC_BF16 ? 1 : 0, nullk, s),
+                     "rope_append")))
+    return rc;
+  if ((rc = attn_launch(d, st, s))) return rc;
+  if ((rc = residual_launch(d, w->wo, H, qd, st->attn, st->x, s))) return rc;
+  if ((rc = launched(dec::launch_rmsnorm_like(st->x, w->ffn_norm, ntype, u, H, d->rms_eps, d->wtype, 1, nullk,
+                                              s),
+                     "rmsnorm_mul")))
+    return rc;
+  a = base_args(d);
+  a.W = w->wgate.w;
+  a.S = w->wgate.scales;
+  a.W2 = w->wup.w;
+  a.S2 = w->wup.scales;
+  a.rows = F;
+  a.cols = H;
+  a.ntask = F;
+  a.in = u;
+  a.y = gate;
+  a.y2 = up;
+  if ((rc = launched(gemv(d->wtype, dec::kEpiStore2, a, s), "gemv_gate_up"))) return rc;
+  if ((rc = launched(dec::launch_swiglu(gate, up, st->h, F, nullk, s), "swiglu"))) return rc;
+  return residual_launch(d, w->wdown, H, F, st->h, st->x, s);
+}
+
+int dec_rope_table(double theta, int32_t head_dim, int32_t max_ctx, float* table, void* stream) {
+  if (!table) return fail(DEC_E_NULL, "table is NULL");
+  if (!(theta > 0.0) || head_dim <= 0 || head_dim % 2 || max_ctx <= 0)
+    return fail(DEC_E_SHAPE, "theta/head_dim/max_ctx");
+  return launched(dec::launch_rope_table(theta, head_dim, max_ctx, table, hipStream_t(stream)), "rope_table");
+}
+
+int dec_embed(const float* embed, int32_t vocab, int32_t hidden, const int32_t* token, float* x,
+              uint32_t* err, void* stream) {
+  if (!embed || !token || !x || !err) return fail(DEC_E_NULL, "embed/token/x/err is NULL");
+  if (vocab <= 0 || hidden <= 0) return fail(DEC_E_SHAPE, "vocab/hidden");
+  return launched(dec::launch_embed(embed, vocab, hidden, token, x, err, hipStream_t(stream)), "embed");
+}
+
+int dec_advance(int32_t* pos, int32_t pos_lo, int32_t pos_hi, const int32_t* tokens, int32_t* token,
+                void* stream) {
+  if (!pos) return fail(DEC_E_NULL, "pos is NULL");
+  if (tokens && !token) return fail(DEC_E_NULL, "token is NULL");
+  if (pos_lo < 0 || pos_hi <= pos_lo) return fail(DEC_E_SHAPE, "pos_lo/pos_hi");
+  return launched(dec::launch_advance(pos, pos_lo, pos_hi, tokens, token, hipStream_t(stream)), "advance");
+}
+
+}  // extern "C"

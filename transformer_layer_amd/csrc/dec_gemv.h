@@ -1,0 +1,293 @@
+// Weight-streaming GEMV core shared by the fused projection kernels.
+//
+// A wavefront owns a column slice of the input vector in registers and
+// streams whole 16-byte "granules" of weight rows with coalesced loads: lane
+// l of a wave reads granule (j*KS + ks)*64 + l of a row, so each load
+// instruction of the wave covers 1 KiB of contiguous weight bytes. A granule
+// is 4 fp32, 8 bf16 or 32 four-bit weights. KS waves (1 or 4) of a workgroup
+// share one task's rows by splitting the columns; their partial dot products
+// meet in LDS. Each lane's dot product is reduced across the wave with DPP
+// row operations.
+//
+// The prologue (PRO_NORM) computes RMSNorm of the input vector and applies
+// the norm weight while staging the slice in registers, so the normalized
+// vector never leaves the chip. The epilogue is selected by EPI:
+//   EPI_STORE     y[r] = W u                                   (per-op path)
+//   EPI_RESIDUAL  x[r] += W u                                  (O / down projection)
+//   EPI_QKV       RoPE on the pair (i, i+d/2) of a head, then q written or k/v
+//                 appended to the cache at position *pos    (QKV projection)
+//   EPI_SWIGLU    h[j] = silu(Wg[j] u) * (Wu[j] u)             (gated FFN)
+//   EPI_STORE2    y[j] = Wg[j] u, y2[j] = Wu[j] u              (per-op gate/up)
+#pragma once
+
+#include "dec_device.h"
+#include "dec_internal.h"
+
+namespace dec {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct WF32 { static constexpr int GE = 4; static constexpr int ID = 0; };
+struct WBF16 { static constexpr int GE = 8; static constexpr int ID = 1; };
+struct WQ4 { static constexpr int GE = 32; static constexpr int ID = 2; };
+
+enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_STORE2 = 4 };
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// partial dot product of one granule with the lane's input values
+template <class T>
+__device__ __forceinline__ float granule_dot(u32x4 w, const float* u, float acc);
+
+template <>
+__device__ __forceinline__ float granule_dot<WF32>(u32x4 w, const float* u, float acc) {
+  acc = fmaf(__uint_as_float(w.x), u[0], acc);
+  acc = fmaf(__uint_as_float(w.y), u[1], acc);
+  acc = fmaf(__uint_as_float(w.z), u[2], acc);
+  acc = fmaf(__uint_as_float(w.w), u[3], acc);
+  return acc;
+}
+
+template <>
+__device__ __forceinline__ float granule_dot<WBF16>(u32x4 w, const float* u, float acc) {
+  acc = fmaf(bf_lo(w.x), u[0], acc);
+  acc = fmaf(bf_hi(w.x), u[1], acc);
+  acc = fmaf(bf_lo(w.y), u[2], acc);
+  acc = fmaf(bf_hi(w.y), u[3], acc);
+  acc = fmaf(bf_lo(w.z), u[4], acc);
+  acc = fmaf(bf_hi(w.z), u[5], acc);
+  acc = fmaf(bf_lo(w.w), u[6], acc);
+  acc = fmaf(bf_hi(w.w), u[7], acc);
+  return acc;
+}
+
+// Four-bit granule: returns sum_e (code_e + 8) * u_e. XOR with 0x8 turns each
+// two's-complement nibble into the unsigned value code + 8; the caller
+// subtracts 8 * sum(u) and applies the block scale.
+__device__ __forceinline__ float q4_dot_offset(u32x4 w, const float* u) {
+  float s = 0.0f;
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t t = words[k] ^ 0x88888888u;
+    const uint32_t lo = t & 0x0f0f0f0fu;          // elements 8k + 0, 2, 4, 6
+    const uint32_t hi = (t >> 4) & 0x0f0f0f0fu;   // elements 8k + 1, 3, 5, 7
+    s = fmaf(float(lo & 0xffu), u[8 * k + 0], s);
+    s = fmaf(float(hi & 0xffu), u[8 * k + 1], s);
+    s = fmaf(float((lo >> 8) & 0xffu), u[8 * k + 2], s);
+    s = fmaf(float((hi >> 8) & 0xffu), u[8 * k + 3], s);
+    s = fmaf(float((lo >> 16) & 0xffu), u[8 * k + 4], s);
+    s = fmaf(float((hi >> 16) & 0xffu), u[8 * k + 5], s);
+    s = fmaf(float(lo >> 24), u[8 * k + 6], s);
+    s = fmaf(float(hi >> 24), u[8 * k + 7], s);
+  }
+  return s;
+}
+
+__device__ __forceinline__ float load_norm_w(const void* g, int ntype, int idx) {
+  return ntype == 1 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(g)[idx])
+                    : reinterpret_cast<const float*>(g)[idx];
+}
+
+template <class T, int NJ, int KS, int EPI>
+__global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
+  constexpr int GE = T::GE;
+  constexpr int NR = 2;  // rows per task
+  constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
+  constexpr int TPW = kWaves / KS;  // tasks per workgroup iteration
+
+  if (a.null_kernel) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int ks = wv % KS;
+  const int slot = wv / KS;
+
+  int pos = 0;
+  if constexpr (EPI == EPI_QKV) {
+    pos = *a.pos;
+    if (pos < 0 || pos >= a.max_ctx) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.err, kErrPos);
+      return;
+    }
+  }
+
+  // ---- prologue: this lane's slice of the input vector, in registers
+  const int G = a.cols / GE;  // granules per row
+  float u[NJ][GE];
+  float usum[NJ];
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int gi = (j * KS + ks) * kWave + lane;
+    const bool ok = gi < G;
+#pragma unroll
+    for (int e = 0; e < GE; e += 4) {
+      float4 v = ok ? *reinterpret_cast<const float4*>(a.in + size_t(gi) * GE + e)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      u[j][e] = v.x; u[j][e + 1] = v.y; u[j][e + 2] = v.z; u[j][e + 3] = v.w;
+    }
+    if constexpr (NORM) {
+#pragma unroll
+      for (int e = 0; e < GE; ++e) ss = fmaf(u[j][e], u[j][e], ss);
+    }
+  }
+  __shared__ float red[kWaves][NR];
+  __shared__ float ssq[kWaves];
+  if constexpr (NORM) {
+    ss = wave_sum(ss);
+    if constexpr (KS > 1) {
+      if (lane == 0) ssq[wv] = ss;
+      __syncthreads();
+      ss = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) ss += ssq[slot * KS + k];
+    }
+    const float r = 1.0f / sqrtf(ss / float(a.cols) + a.eps);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int gi = (j * KS + ks) * kWave + lane;
+      const bool ok = gi < G;
+#pragma unroll
+      for (int e = 0; e < GE; ++e)
+        u[j][e] = ok ? (u[j][e] * r) * load_norm_w(a.norm, a.ntype, gi * GE + e) : 0.0f;
+    }
+  }
+  if constexpr (T::ID == 2) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < GE; ++e) s += u[j][e];
+      usum[j] = 8.0f * s;
+    }
+  }
+
+  const size_t row_bytes = (T::ID == 2) ? size_t(a.cols) / 2 : size_t(a.cols) * (T::ID == 0 ? 4 : 2);
+  const int half = a.d / 2;
+
+  // ---- tasks
+  for (int base = blockIdx.x * TPW; base < a.ntask; base += gridDim.x * TPW) {
+    const int task = base + slot;
+    const bool tvalid = task < a.ntask;
+    // the two rows of this task, and the matrix each comes from
+    int r0, r1;
+    const uint8_t* W0 = reinterpret_cast<const uint8_t*>(a.W);
+    const uint8_t* W1 = W0;
+    const __half* S0 = reinterpret_cast<const __half*>(a.S);
+    const __half* S1 = S0;
+    if constexpr (EPI == EPI_QKV) {
+      r0 = (task / half) * a.d + (task % half);
+      r1 = r0 + half;
+    } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_STORE2) {
+      r0 = task;
+      r1 = task;
+      W1 = reinterpret_cast<const uint8_t*>(a.W2);
+      S1 = reinterpret_cast<const __half*>(a.S2);
+    } else {
+      r0 = task * NR;
+      r1 = r0 + 1;
+    }
+    const bool v0 = tvalid && r0 < a.rows;
+    const bool v1 = tvalid && r1 < a.rows;
+
+    u32x4 wq[NR][NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int gi = (j * KS + ks) * kWave + lane;
+      const bool ok = gi < G;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      wq[0][j] = (ok && v0) ? ldg16(W0 + size_t(r0) * row_bytes + size_t(gi) * 16) : z;
+      wq[1][j] = (ok && v1) ? ldg16(W1 + size_t(r1) * row_bytes + size_t(gi) * 16) : z;
+    }
+    float acc[NR] = {0.0f, 0.0f};
+    if constexpr (T::ID == 2) {
+      float sc[NR][NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int gi = (j * KS + ks) * kWave + lane;
+        const bool ok = gi < G;
+        sc[0][j] = (ok && v0) ? __half2float(S0[size_t(r0) * G + gi]) : 0.0f;
+        sc[1][j] = (ok && v1) ? __half2float(S1[size_t(r1) * G + gi]) : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < NR; ++k)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[k] = fmaf(sc[k][j], q4_dot_offset(wq[k][j], u[j]) - usum[j], acc[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NR; ++k)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[k] = granule_dot<T>(wq[k][j], u[j], acc[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < NR; ++k) acc[k] = wave_sum(acc[k]);
+    if constexpr (KS > 1) {
+      if (lane == 0) { red[wv][0] = acc[0]; red[wv][1] = acc[1]; }
+      __syncthreads();
+      if (ks == 0) {
+        acc[0] = 0.0f; acc[1] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) { acc[0] += red[slot * KS + k][0]; acc[1] += red[slot * KS + k][1]; }
+      }
+      __syncthreads();
+    }
+
+    // ---- epilogue (one lane per task)
+    if (ks == 0 && lane == 0 && tvalid) {
+      if constexpr (EPI == EPI_STORE) {
+        if (v0) a.y[r0] = acc[0];
+        if (v1) a.y[r1] = acc[1];
+      } else if constexpr (EPI == EPI_RESIDUAL) {
+        if (v0) a.x[r0] += acc[0];
+        if (v1) a.x[r1] += acc[1];
+      } else if constexpr (EPI == EPI_SWIGLU) {
+        a.y[r0] = swiglu(acc[0], acc[1]);
+      } else if constexpr (EPI == EPI_STORE2) {
+        a.y[r0] = acc[0];
+        a.y2[r0] = acc[1];
+      } else {  // EPI_QKV
+        const int head = task / half;
+        const int i = task % half;
+        float y0 = acc[0], y1 = acc[1];
+        if (head < a.nq + a.nkv) {
+          const float c = a.rope[(size_t(pos) * half + i) * 2];
+          const float s = a.rope[(size_t(pos) * half + i) * 2 + 1];
+          rope_rotate(y0, y1, c, s);
+        }
+        if (head < a.nq) {
+          a.y[r0] = y0;
+          a.y[r1] = y1;
+        } else {
+          const bool isk = head < a.nq + a.nkv;
+          const int j = isk ? head - a.nq : head - a.nq - a.nkv;
+          const size_t off = (size_t(j) * a.max_ctx + pos) * a.d + i;
+          void* cache = isk ? a.kc : a.vc;
+          if (a.kvtype == 1) {
+            uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
+            c16[off] = f32_to_bf16(y0);
+            c16[off + half] = f32_to_bf16(y1);
+          } else {
+            float* c32 = reinterpret_cast<float*>(cache);
+            c32[off] = y0;
+            c32[off + half] = y1;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Number of granules per lane for a row of `cols` elements split over KS waves.
+inline int gemv_nj(int cols, int ge, int ks) {
+  const int G = cols / ge;
+  return (G + kWave * ks - 1) / (kWave * ks);
+}
+
+// Waves that share one row: 1 while a lane's input slice fits in 64
+// registers, else 4 (columns split four ways, partial sums meet in LDS).
+inline int gemv_ks(int cols, int ge) { return gemv_nj(cols, ge, 1) * ge <= 64 ? 1 : 4; }
+
+}  // namespace dec

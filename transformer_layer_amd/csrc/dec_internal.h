@@ -1,0 +1,80 @@
+// Internal launch interface between the C ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dec {
+
+constexpr uint32_t kErrPos = 0x1u;
+constexpr uint32_t kErrToken = 0x2u;
+
+// Arguments of the GEMV-core kernels (passed by value).
+struct GemvArgs {
+  const void* W;       // first matrix (elements)
+  const void* S;       // its fp16 block scales (4-bit weights only)
+  const void* W2;      // second matrix (gate/up pair) or null
+  const void* S2;
+  int rows;            // rows of the matrix / matrices
+  int cols;            // input length
+  int ntask;           // tasks (two rows each)
+  const float* in;     // input vector [cols]
+  const void* norm;    // RMSNorm weight [cols] (norm prologue only)
+  int ntype;           // 0 f32, 1 bf16
+  float eps;
+  float* y;            // outputs, by epilogue
+  float* y2;
+  float* x;
+  // QKV epilogue
+  int nq, nkv, d, max_ctx, kvtype;
+  const int32_t* pos;
+  const float* rope;
+  void* kc;
+  void* vc;
+  uint32_t* err;
+  int null_kernel;
+};
+
+enum GemvEpi { kEpiStore = 0, kEpiResidual = 1, kEpiQkv = 2, kEpiSwiglu = 3, kEpiStore2 = 4 };
+
+// Launch the GEMV core for weight type wtype (0 f32, 1 bf16, 2 q4).
+hipError_t launch_gemv_f32(int epi, const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_bf16(int epi, const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_q4(int epi, const GemvArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const float* q;      // [n_q d]
+  const void* kc;      // [n_kv][max_ctx][d]
+  const void* vc;
+  float* part;         // [n_kv][S][g][d + 2]
+  uint32_t* counters;  // [n_kv]
+  float* out;          // [n_q d]
+  const int32_t* pos;
+  uint32_t* err;
+  int nq, nkv, d, max_ctx, chunk, nsplit, kvtype;
+  int null_kernel;
+};
+
+// attention chunk (positions per split) and split count for a shape
+void attn_plan(int n_kv, int max_ctx, int chunk_req, int* chunk, int* nsplit);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+// small per-op and per-token kernels
+// RMSNorm (optionally times its weight) with the fused kernels' summation
+// order for weight type `wtype`.
+hipError_t launch_rmsnorm_like(const float* x, const void* g, int ntype, float* out, int n,
+                               float eps, int wtype, int with_weight, int null_kernel,
+                               hipStream_t s);
+hipError_t launch_mul(float* u, const void* g, int ntype, int n, int null_kernel, hipStream_t s);
+hipError_t launch_rope_append(const float* y, float* q, void* kc, void* vc, const int32_t* pos,
+                              const float* rope, uint32_t* err, int nq, int nkv, int d, int max_ctx,
+                              int kvtype, int null_kernel, hipStream_t s);
+hipError_t launch_swiglu(const float* g, const float* u, float* h, int n, int null_kernel,
+                         hipStream_t s);
+hipError_t launch_rope_table(double theta, int d, int max_ctx, float* table, hipStream_t s);
+hipError_t launch_embed(const float* embed, int vocab, int hidden, const int32_t* token, float* x,
+                        uint32_t* err, hipStream_t s);
+hipError_t launch_advance(int32_t* pos, int pos_lo, int pos_hi, const int32_t* tokens,
+                          int32_t* token, hipStream_t s);
+
+}  // namespace dec
