@@ -3,11 +3,18 @@
 // Grid: n_kv * nsplit workgroups, split-major (block b serves kv head
 // b % n_kv and split b / n_kv), so the splits that hold cache positions come
 // first and the ones past the current position exit at once. A workgroup
-// streams its chunk of K once to score all query heads of its kv head, turns
-// the scores into exp(s - m) in LDS, streams the same chunk of V once, and
-// writes (m, l, o) partials. The last workgroup of a kv head to arrive
-// (device-scope counter) combines the partials with a log-sum-exp rescale and
-// resets the counter, so the kernel replays unchanged inside a graph.
+// reads its chunk of K once to score every query head of its kv head (scores
+// kept in LDS, in log2 units), turns them into exp2(s - m) with one
+// exponential per (head, position), reads the same chunk of V once, and
+// writes the split's partials: o (unnormalized) and (m, l). The first batch
+// of V rows is requested together with K.
+//
+// The last workgroup of a kv head to arrive combines the partials with a
+// log-sum-exp rescale. Ordering: every lane waits for its own partial stores
+// to complete, the workgroup meets at a barrier, and one thread performs an
+// agent-scope acquire-release increment of the head's counter; the last
+// arriver acquires at agent scope before reading. The combiner resets the
+// counter, so the kernel replays unchanged inside a graph.
 #include "dec_device.h"
 #include "dec_internal.h"
 
@@ -17,6 +24,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunkMax = 256;  // cache positions per split
 constexpr int kSplitMax = 256;  // splits per kv head
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <int KVT>
 __device__ __forceinline__ void unpack_row(u32x4 v, float* f) {
@@ -36,7 +44,7 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   constexpr int LPR = D / DPL;          // lanes per cache row
   constexpr int RPW = kWave / LPR;      // rows per wave load
   constexpr int RPS = RPW * kWaves;     // rows per workgroup step
-  constexpr int U = 4;                  // row steps in flight
+  constexpr int U = 8;                  // row steps in flight per batch
   static_assert(LPR >= 2 && LPR <= 32, "row layout");
 
   if (a.null_kernel) return;
@@ -53,45 +61,59 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   const int t0 = s * a.chunk;
   const int t1 = min(t0 + a.chunk, L);
   const int n = t1 - t0;
+  const int nsteps = (n + RPS - 1) / RPS;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int sub = lane / LPR;
   const int li = lane % LPR;
   const int d0 = li * DPL;
-  const float scale = 1.0f / sqrtf(float(D));
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.kc) + size_t(j) * a.max_ctx * D * EB;
+  const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.vc) + size_t(j) * a.max_ctx * D * EB;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  auto row = [&](int step) { return t0 + step * RPS + wv * RPW + sub; };
+
+  // first batch of K and V rows, then the queries
+  u32x4 kv[U], vv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int t = row(u);
+    const bool ok = u < nsteps && t < t1;
+    kv[u] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + d0) * EB) : z;
+    vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
+  }
+  const float qscale = kLog2e / sqrtf(float(D));
+  float qv[G][DPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < DPL; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(a.q + (j * G + hh) * D + d0 + e);
+      qv[hh][e] = x.x * qscale; qv[hh][e + 1] = x.y * qscale;
+      qv[hh][e + 2] = x.z * qscale; qv[hh][e + 3] = x.w * qscale;
+    }
 
   __shared__ float sc[G][kChunkMax];
   __shared__ float stat[G][2];
   __shared__ float ored[kWaves][G][D];
   __shared__ int last;
 
-  float qv[G][DPL];
+  // ---- scores (log2 units): s_t = (q . k_t) log2(e) / sqrt(d)
+  for (int b = 0; b < nsteps; b += U) {
+    if (b > 0) {
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) qv[hh][e] = a.q[(j * G + hh) * D + d0 + e] * scale;
-
-  const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.kc) + size_t(j) * a.max_ctx * D * EB;
-  const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.vc) + size_t(j) * a.max_ctx * D * EB;
-  const int nsteps = (n + RPS - 1) / RPS;
-
-  // ---- scores: s_t = (q . k_t) / sqrt(d) for every query head of the group
-  for (int it = 0; it < nsteps; it += U) {
-    u32x4 kv[U];
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      const int t = t0 + (it + uu) * RPS + wv * RPW + sub;
-      const bool ok = (it + uu < nsteps) && t < t1;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kv[uu] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + d0) * EB) : z;
+      for (int u = 0; u < U; ++u) {
+        const int t = row(b + u);
+        const bool ok = b + u < nsteps && t < t1;
+        kv[u] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + d0) * EB) : z;
+      }
     }
 #pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      const int t = t0 + (it + uu) * RPS + wv * RPW + sub;
-      const bool ok = (it + uu < nsteps) && t < t1;
+    for (int u = 0; u < U; ++u) {
+      const int t = row(b + u);
+      const bool ok = b + u < nsteps && t < t1;
       float kf[DPL];
-      unpack_row<KVT>(kv[uu], kf);
+      unpack_row<KVT>(kv[u], kf);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float p = 0.0f;
@@ -104,14 +126,14 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- per-head max and sum of exp over the chunk
+  // ---- per head: m = max s, p = exp2(s - m), l = sum p (one exponential per entry)
   for (int hh = wv; hh < G; hh += kWaves) {
     float m = -INFINITY;
     for (int i = lane; i < n; i += kWave) m = fmaxf(m, sc[hh][i]);
     m = wave_max(m);
     float l = 0.0f;
     for (int i = lane; i < n; i += kWave) {
-      const float p = expf(sc[hh][i] - m);
+      const float p = exp2f(sc[hh][i] - m);
       sc[hh][i] = p;
       l += p;
     }
@@ -126,22 +148,21 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   for (int hh = 0; hh < G; ++hh)
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[hh][e] = 0.0f;
-  for (int it = 0; it < nsteps; it += U) {
-    u32x4 vv[U];
+  for (int b = 0; b < nsteps; b += U) {
+    if (b > 0) {
 #pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      const int t = t0 + (it + uu) * RPS + wv * RPW + sub;
-      const bool ok = (it + uu < nsteps) && t < t1;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      vv[uu] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
+      for (int u = 0; u < U; ++u) {
+        const int t = row(b + u);
+        const bool ok = b + u < nsteps && t < t1;
+        vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
+      }
     }
 #pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      const int t = t0 + (it + uu) * RPS + wv * RPW + sub;
-      const bool ok = (it + uu < nsteps) && t < t1;
-      if (ok) {
+    for (int u = 0; u < U; ++u) {
+      const int t = row(b + u);
+      if (b + u < nsteps && t < t1) {
         float vf[DPL];
-        unpack_row<KVT>(vv[uu], vf);
+        unpack_row<KVT>(vv[u], vf);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
           const float p = sc[hh][t - t0];
@@ -165,71 +186,101 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
       for (int e = 0; e < DPL; ++e) ored[wv][hh][d0 + e] = o[hh][e];
   __syncthreads();
 
-  // ---- partials (m, l, o) of this split
-  constexpr int PS = D + 2;
-  float* pp = a.part + (size_t(j) * a.nsplit + s) * G * PS;
+  // ---- this split's partials: o [j][s][G][D] and (m, l) [j][s][G][2]
+  float* po = a.part + (size_t(j) * a.nsplit + s) * G * D;
+  float* pml = a.part + size_t(a.nkv) * a.nsplit * G * D + (size_t(j) * a.nsplit + s) * G * 2;
   for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
     const int hh = idx / D, dd = idx % D;
-    pp[hh * PS + dd] = ((ored[0][hh][dd] + ored[1][hh][dd]) + ored[2][hh][dd]) + ored[3][hh][dd];
+    po[idx] = ((ored[0][hh][dd] + ored[1][hh][dd]) + ored[2][hh][dd]) + ored[3][hh][dd];
   }
   if (threadIdx.x < G) {
-    pp[threadIdx.x * PS + D] = stat[threadIdx.x][0];
-    pp[threadIdx.x * PS + D + 1] = stat[threadIdx.x][1];
+    pml[threadIdx.x * 2] = stat[threadIdx.x][0];
+    pml[threadIdx.x * 2 + 1] = stat[threadIdx.x][1];
   }
 
   // ---- arrival: the last split of this kv head combines
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);  // this lane's partial stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&a.counters[j], 1u);
+    const unsigned prev =
+        __hip_atomic_fetch_add(&a.counters[j], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     last = (prev == unsigned(ns - 1));
   }
   __syncthreads();
   if (!last) return;
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
+  // per (split, head): weight w = exp2(m - M) and the denominator sum w l
   __shared__ float wts[kSplitMax][G];
   __shared__ float den[G];
-  const float* pj = a.part + size_t(j) * a.nsplit * G * PS;
+  const float* pj = a.part + size_t(j) * a.nsplit * G * D;
+  const float* mlj = a.part + size_t(a.nkv) * a.nsplit * G * D + size_t(j) * a.nsplit * G * 2;
   for (int hh = wv; hh < G; hh += kWaves) {
     float M = -INFINITY;
-    for (int t = lane; t < ns; t += kWave) M = fmaxf(M, pj[(size_t(t) * G + hh) * PS + D]);
+    for (int t = lane; t < ns; t += kWave) M = fmaxf(M, mlj[(t * G + hh) * 2]);
     M = wave_max(M);
     float dsum = 0.0f;
     for (int t = lane; t < ns; t += kWave) {
-      const float* e = pj + (size_t(t) * G + hh) * PS;
-      const float w = expf(e[D] - M);
+      const float w = exp2f(mlj[(t * G + hh) * 2] - M);
       wts[t][hh] = w;
-      dsum = fmaf(w, e[D + 1], dsum);
+      dsum = fmaf(w, mlj[(t * G + hh) * 2 + 1], dsum);
     }
     dsum = wave_sum(dsum);
     if (lane == 0) den[hh] = dsum;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
-    const int hh = idx / D, dd = idx % D;
-    const float* e = pj + hh * PS + dd;
-    float acc = 0.0f;
-    int t = 0;
-    for (; t + 8 <= ns; t += 8) {
-      float v[8];
+  // outputs as float4 groups; each thread sums a strided subset of the splits
+  constexpr int NV = G * D / 4;                 // float4 outputs
+  constexpr int PARTS = kBlock / NV > 0 ? kBlock / NV : 1;
+  __shared__ float4 accs[PARTS > 1 ? PARTS : 1][NV];
+  for (int f = threadIdx.x % NV; f < NV; f += kBlock) {
+    const int part = threadIdx.x / NV;
+    if (part >= PARTS) break;
+    const int hh = (f * 4) / D;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int t = part;
+    for (; t + 3 * PARTS < ns; t += 4 * PARTS) {
+      float4 v[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = e[size_t(t + k) * G * PS];
+      for (int k = 0; k < 4; ++k) v[k] = reinterpret_cast<const float4*>(pj + size_t(t + k * PARTS) * G * D)[f];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc = fmaf(v[k], wts[t + k][hh], acc);
+      for (int k = 0; k < 4; ++k) {
+        const float w = wts[t + k * PARTS][hh];
+        acc.x = fmaf(v[k].x, w, acc.x); acc.y = fmaf(v[k].y, w, acc.y);
+        acc.z = fmaf(v[k].z, w, acc.z); acc.w = fmaf(v[k].w, w, acc.w);
+      }
     }
-    for (; t < ns; ++t) acc = fmaf(e[size_t(t) * G * PS], wts[t][hh], acc);
-    a.out[(j * G + hh) * D + dd] = acc / den[hh];
+    for (; t < ns; t += PARTS) {
+      const float4 v = reinterpret_cast<const float4*>(pj + size_t(t) * G * D)[f];
+      const float w = wts[t][hh];
+      acc.x = fmaf(v.x, w, acc.x); acc.y = fmaf(v.y, w, acc.y);
+      acc.z = fmaf(v.z, w, acc.z); acc.w = fmaf(v.w, w, acc.w);
+    }
+    accs[part][f] = acc;
   }
-  if (threadIdx.x == 0) atomicExch(&a.counters[j], 0u);
+  __syncthreads();
+  for (int f = threadIdx.x; f < NV; f += kBlock) {
+    const int hh = (f * 4) / D;
+    float4 acc = accs[0][f];
+    for (int p = 1; p < PARTS; ++p) {
+      const float4 v = accs[p][f];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    const float r = 1.0f / den[hh];
+    reinterpret_cast<float4*>(a.out + j * G * D)[f] = make_float4(acc.x * r, acc.y * r, acc.z * r, acc.w * r);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&a.counters[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 void attn_plan(int n_kv, int max_ctx, int chunk_req, int* chunk, int* nsplit) {
   int c = chunk_req;
   if (c <= 0) {
-    // aim at about 768 workgroups over the whole cache
-    const long target = 768;
-    c = int((long(max_ctx) * n_kv + target - 1) / target);
+    // about two workgroups per compute unit over the whole cache, at most
+    // 64 splits per kv head, chunks a multiple of 16 rows
+    int splits = 512 / n_kv;
+    if (splits > 64) splits = 64;
+    if (splits < 1) splits = 1;
+    c = (max_ctx + splits - 1) / splits;
     c = ((c + 15) / 16) * 16;
   }
   const int cmin = (max_ctx + kSplitMax - 1) / kSplitMax;

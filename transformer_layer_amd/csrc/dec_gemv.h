@@ -86,9 +86,30 @@ __device__ __forceinline__ float q4_dot_offset(u32x4 w, const float* u) {
   return s;
 }
 
-__device__ __forceinline__ float load_norm_w(const void* g, int ntype, int idx) {
-  return ntype == 1 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(g)[idx])
-                    : reinterpret_cast<const float*>(g)[idx];
+// GE norm-weight values of granule gi (f32 or bf16), with 16-byte loads.
+template <int GE>
+__device__ __forceinline__ void load_norm_granule(const void* g, int ntype, int gi, float* out) {
+  if (ntype == 1) {
+    const uint8_t* b = reinterpret_cast<const uint8_t*>(g) + size_t(gi) * GE * 2;
+    if constexpr (GE == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(b);
+      out[0] = bf_lo(v.x); out[1] = bf_hi(v.x); out[2] = bf_lo(v.y); out[3] = bf_hi(v.y);
+    } else {
+#pragma unroll
+      for (int e = 0; e < GE; e += 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(b + e * 2);
+        out[e + 0] = bf_lo(v.x); out[e + 1] = bf_hi(v.x); out[e + 2] = bf_lo(v.y); out[e + 3] = bf_hi(v.y);
+        out[e + 4] = bf_lo(v.z); out[e + 5] = bf_hi(v.z); out[e + 6] = bf_lo(v.w); out[e + 7] = bf_hi(v.w);
+      }
+    }
+  } else {
+    const float* f = reinterpret_cast<const float*>(g) + size_t(gi) * GE;
+#pragma unroll
+    for (int e = 0; e < GE; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(f + e);
+      out[e] = v.x; out[e + 1] = v.y; out[e + 2] = v.z; out[e + 3] = v.w;
+    }
+  }
 }
 
 template <class T, int NJ, int KS, int EPI>
@@ -96,6 +117,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
   constexpr int GE = T::GE;
   constexpr int NR = 2;  // rows per task
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
+  constexpr bool Q4 = (T::ID == 2);
   constexpr int TPW = kWaves / KS;  // tasks per workgroup iteration
 
   if (a.null_kernel) return;
@@ -113,8 +135,55 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
     }
   }
 
-  // ---- prologue: this lane's slice of the input vector, in registers
   const int G = a.cols / GE;  // granules per row
+  const size_t row_bytes = Q4 ? size_t(a.cols) / 2 : size_t(a.cols) * (T::ID == 0 ? 4 : 2);
+  const int half = a.d / 2;
+  const uint8_t* Wa = reinterpret_cast<const uint8_t*>(a.W);
+  const uint8_t* Wb = (EPI == EPI_SWIGLU || EPI == EPI_STORE2) ? reinterpret_cast<const uint8_t*>(a.W2) : Wa;
+  const __half* Sa = reinterpret_cast<const __half*>(a.S);
+  const __half* Sb = (EPI == EPI_SWIGLU || EPI == EPI_STORE2) ? reinterpret_cast<const __half*>(a.S2) : Sa;
+
+  // the two rows of a task (each from matrix a or b)
+  auto rows_of = [&](int task, int& r0, int& r1) {
+    if constexpr (EPI == EPI_QKV) {
+      r0 = (task / half) * a.d + (task % half);
+      r1 = r0 + half;
+    } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_STORE2) {
+      r0 = task;
+      r1 = task;
+    } else {
+      r0 = task * NR;
+      r1 = r0 + 1;
+    }
+  };
+  // weights (and 4-bit block scales) of a task's rows
+  auto load_task = [&](int task, u32x4 (&wq)[NR][NJ], float (&sc)[NR][NJ]) {
+    int r0, r1;
+    rows_of(task, r0, r1);
+    const bool v0 = task < a.ntask && r0 < a.rows;
+    const bool v1 = task < a.ntask && r1 < a.rows;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int gi = (j * KS + ks) * kWave + lane;
+      const bool ok = gi < G;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      wq[0][j] = (ok && v0) ? ldg16(Wa + size_t(r0) * row_bytes + size_t(gi) * 16) : z;
+      wq[1][j] = (ok && v1) ? ldg16(Wb + size_t(r1) * row_bytes + size_t(gi) * 16) : z;
+      if constexpr (Q4) {
+        sc[0][j] = (ok && v0) ? __half2float(Sa[size_t(r0) * G + gi]) : 0.0f;
+        sc[1][j] = (ok && v1) ? __half2float(Sb[size_t(r1) * G + gi]) : 0.0f;
+      }
+    }
+  };
+
+  // the first task's weights do not depend on the input: fetch them while
+  // the prologue reads and normalizes the input vector
+  const int stride = gridDim.x * TPW;
+  u32x4 wq[NR][NJ];
+  float sc[NR][NJ];
+  load_task(blockIdx.x * TPW + slot, wq, sc);
+
+  // ---- prologue: this lane's slice of the input vector, in registers
   float u[NJ][GE];
   float usum[NJ];
   float ss = 0.0f;
@@ -133,7 +202,8 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
       for (int e = 0; e < GE; ++e) ss = fmaf(u[j][e], u[j][e], ss);
     }
   }
-  __shared__ float red[kWaves][NR];
+  constexpr int kBatch = 16;  // tasks per LDS batch (column-split waves)
+  __shared__ float red[kWaves][kBatch][NR];
   __shared__ float ssq[kWaves];
   if constexpr (NORM) {
     ss = wave_sum(ss);
@@ -148,13 +218,18 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int gi = (j * KS + ks) * kWave + lane;
-      const bool ok = gi < G;
+      float g[GE];
+      if (gi < G) {
+        load_norm_granule<GE>(a.norm, a.ntype, gi, g);
+      } else {
 #pragma unroll
-      for (int e = 0; e < GE; ++e)
-        u[j][e] = ok ? (u[j][e] * r) * load_norm_w(a.norm, a.ntype, gi * GE + e) : 0.0f;
+        for (int e = 0; e < GE; ++e) g[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < GE; ++e) u[j][e] = (u[j][e] * r) * g[e];
     }
   }
-  if constexpr (T::ID == 2) {
+  if constexpr (Q4) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       float s = 0.0f;
@@ -164,53 +239,67 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
     }
   }
 
-  const size_t row_bytes = (T::ID == 2) ? size_t(a.cols) / 2 : size_t(a.cols) * (T::ID == 0 ? 4 : 2);
-  const int half = a.d / 2;
+  // ---- epilogue of one task (run by one lane)
+  auto epilogue = [&](int task, float y0, float y1) {
+    int r0, r1;
+    rows_of(task, r0, r1);
+    const bool v0 = r0 < a.rows;
+    const bool v1 = r1 < a.rows;
+    if constexpr (EPI == EPI_STORE) {
+      if (v0) a.y[r0] = y0;
+      if (v1) a.y[r1] = y1;
+    } else if constexpr (EPI == EPI_RESIDUAL) {
+      if (v0) a.x[r0] += y0;
+      if (v1) a.x[r1] += y1;
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      a.y[r0] = swiglu(y0, y1);
+    } else if constexpr (EPI == EPI_STORE2) {
+      a.y[r0] = y0;
+      a.y2[r0] = y1;
+    } else {  // EPI_QKV
+      const int head = task / half;
+      const int i = task % half;
+      if (head < a.nq + a.nkv) {
+        const float c = a.rope[(size_t(pos) * half + i) * 2];
+        const float s = a.rope[(size_t(pos) * half + i) * 2 + 1];
+        rope_rotate(y0, y1, c, s);
+      }
+      if (head < a.nq) {
+        a.y[r0] = y0;
+        a.y[r1] = y1;
+      } else {
+        const bool isk = head < a.nq + a.nkv;
+        const int j = isk ? head - a.nq : head - a.nq - a.nkv;
+        const size_t off = (size_t(j) * a.max_ctx + pos) * a.d + i;
+        void* cache = isk ? a.kc : a.vc;
+        if (a.kvtype == 1) {
+          uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
+          c16[off] = f32_to_bf16(y0);
+          c16[off + half] = f32_to_bf16(y1);
+        } else {
+          float* c32 = reinterpret_cast<float*>(cache);
+          c32[off] = y0;
+          c32[off + half] = y1;
+        }
+      }
+    }
+  };
 
-  // ---- tasks
-  for (int base = blockIdx.x * TPW; base < a.ntask; base += gridDim.x * TPW) {
+  // ---- tasks: this wave slot handles task, task + stride, ...; the next
+  // task's weights are in flight while the current one is reduced
+  int nb = 0;                                // tasks in the current LDS batch
+  int batch_base = blockIdx.x * TPW;         // base of its first task
+  for (int base = blockIdx.x * TPW; base < a.ntask; base += stride) {
     const int task = base + slot;
     const bool tvalid = task < a.ntask;
-    // the two rows of this task, and the matrix each comes from
-    int r0, r1;
-    const uint8_t* W0 = reinterpret_cast<const uint8_t*>(a.W);
-    const uint8_t* W1 = W0;
-    const __half* S0 = reinterpret_cast<const __half*>(a.S);
-    const __half* S1 = S0;
-    if constexpr (EPI == EPI_QKV) {
-      r0 = (task / half) * a.d + (task % half);
-      r1 = r0 + half;
-    } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_STORE2) {
-      r0 = task;
-      r1 = task;
-      W1 = reinterpret_cast<const uint8_t*>(a.W2);
-      S1 = reinterpret_cast<const __half*>(a.S2);
-    } else {
-      r0 = task * NR;
-      r1 = r0 + 1;
-    }
-    const bool v0 = tvalid && r0 < a.rows;
-    const bool v1 = tvalid && r1 < a.rows;
 
-    u32x4 wq[NR][NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int gi = (j * KS + ks) * kWave + lane;
-      const bool ok = gi < G;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      wq[0][j] = (ok && v0) ? ldg16(W0 + size_t(r0) * row_bytes + size_t(gi) * 16) : z;
-      wq[1][j] = (ok && v1) ? ldg16(W1 + size_t(r1) * row_bytes + size_t(gi) * 16) : z;
-    }
+    u32x4 wn[NR][NJ];
+    float sn[NR][NJ];
+    const bool more = base + stride < a.ntask;
+    if (more) load_task(task + stride, wn, sn);
+
     float acc[NR] = {0.0f, 0.0f};
-    if constexpr (T::ID == 2) {
-      float sc[NR][NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int gi = (j * KS + ks) * kWave + lane;
-        const bool ok = gi < G;
-        sc[0][j] = (ok && v0) ? __half2float(S0[size_t(r0) * G + gi]) : 0.0f;
-        sc[1][j] = (ok && v1) ? __half2float(S1[size_t(r1) * G + gi]) : 0.0f;
-      }
+    if constexpr (Q4) {
 #pragma unroll
       for (int k = 0; k < NR; ++k)
 #pragma unroll
@@ -222,72 +311,61 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[k] = granule_dot<T>(wq[k][j], u[j], acc[k]);
     }
+    if (more) {
+#pragma unroll
+      for (int k = 0; k < NR; ++k)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          wq[k][j] = wn[k][j];
+          if constexpr (Q4) sc[k][j] = sn[k][j];
+        }
+    }
 #pragma unroll
     for (int k = 0; k < NR; ++k) acc[k] = wave_sum(acc[k]);
-    if constexpr (KS > 1) {
-      if (lane == 0) { red[wv][0] = acc[0]; red[wv][1] = acc[1]; }
-      __syncthreads();
-      if (ks == 0) {
-        acc[0] = 0.0f; acc[1] = 0.0f;
+    if constexpr (KS == 1) {
+      if (lane == 0 && tvalid) epilogue(task, acc[0], acc[1]);
+    } else {
+      // partial sums of the KS waves meet in LDS; finished in batches so the
+      // waves do not meet at a barrier for every task
+      if (lane == 0) { red[wv][nb][0] = acc[0]; red[wv][nb][1] = acc[1]; }
+      ++nb;
+      if (nb == kBatch || base + stride >= a.ntask) {
+        __syncthreads();
+        if (ks == 0 && lane < nb) {
+          const int t = batch_base + lane * stride + slot;
+          if (t < a.ntask) {
+            float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) { acc[0] += red[slot * KS + k][0]; acc[1] += red[slot * KS + k][1]; }
-      }
-      __syncthreads();
-    }
-
-    // ---- epilogue (one lane per task)
-    if (ks == 0 && lane == 0 && tvalid) {
-      if constexpr (EPI == EPI_STORE) {
-        if (v0) a.y[r0] = acc[0];
-        if (v1) a.y[r1] = acc[1];
-      } else if constexpr (EPI == EPI_RESIDUAL) {
-        if (v0) a.x[r0] += acc[0];
-        if (v1) a.x[r1] += acc[1];
-      } else if constexpr (EPI == EPI_SWIGLU) {
-        a.y[r0] = swiglu(acc[0], acc[1]);
-      } else if constexpr (EPI == EPI_STORE2) {
-        a.y[r0] = acc[0];
-        a.y2[r0] = acc[1];
-      } else {  // EPI_QKV
-        const int head = task / half;
-        const int i = task % half;
-        float y0 = acc[0], y1 = acc[1];
-        if (head < a.nq + a.nkv) {
-          const float c = a.rope[(size_t(pos) * half + i) * 2];
-          const float s = a.rope[(size_t(pos) * half + i) * 2 + 1];
-          rope_rotate(y0, y1, c, s);
-        }
-        if (head < a.nq) {
-          a.y[r0] = y0;
-          a.y[r1] = y1;
-        } else {
-          const bool isk = head < a.nq + a.nkv;
-          const int j = isk ? head - a.nq : head - a.nq - a.nkv;
-          const size_t off = (size_t(j) * a.max_ctx + pos) * a.d + i;
-          void* cache = isk ? a.kc : a.vc;
-          if (a.kvtype == 1) {
-            uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
-            c16[off] = f32_to_bf16(y0);
-            c16[off + half] = f32_to_bf16(y1);
-          } else {
-            float* c32 = reinterpret_cast<float*>(cache);
-            c32[off] = y0;
-            c32[off + half] = y1;
+            for (int k = 0; k < KS; ++k) { s0 += red[slot * KS + k][lane][0]; s1 += red[slot * KS + k][lane][1]; }
+            epilogue(t, s0, s1);
           }
         }
+        __syncthreads();
+        nb = 0;
+        batch_base = base + stride;
       }
     }
   }
 }
 
-// Number of granules per lane for a row of `cols` elements split over KS waves.
-inline int gemv_nj(int cols, int ge, int ks) {
-  const int G = cols / ge;
-  return (G + kWave * ks - 1) / (kWave * ks);
+// Workgroups for `groups` task groups: at most what the device keeps resident
+// (occupancy x compute units), with the groups spread evenly over them.
+template <class K>
+inline int gemv_grid(K kernel, int groups) {
+  static thread_local int resident[64] = {0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int& cap = resident[dev & 63];
+  if (cap == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    cap = per_cu * cus;
+  }
+  const int per_wg = (groups + cap - 1) / cap;
+  return (groups + per_wg - 1) / per_wg;
 }
-
-// Waves that share one row: 1 while a lane's input slice fits in 64
-// registers, else 4 (columns split four ways, partial sums meet in LDS).
-inline int gemv_ks(int cols, int ge) { return gemv_nj(cols, ge, 1) * ge <= 64 ? 1 : 4; }
 
 }  // namespace dec

@@ -3,44 +3,48 @@
 
 namespace dec {
 
-template <int NJ, int KS>
-static hipError_t go_bf16(int epi, const GemvArgs& a, hipStream_t s) {
+template <int NJ, int KS, int EPI>
+static hipError_t go_bf16_epi(const GemvArgs& a, hipStream_t s) {
+  auto kernel = gemv_kernel<WBF16, NJ, KS, EPI>;
   const int tpw = kWaves / KS;
-  const int grid = (a.ntask + tpw - 1) / tpw;
-  if (grid <= 0) return hipSuccess;
-  switch (epi) {
-    case kEpiStore:
-      hipLaunchKernelGGL((gemv_kernel<WBF16, NJ, KS, EPI_STORE>), dim3(grid), dim3(kBlock), 0, s, a);
-      break;
-    case kEpiResidual:
-      hipLaunchKernelGGL((gemv_kernel<WBF16, NJ, KS, EPI_RESIDUAL>), dim3(grid), dim3(kBlock), 0, s, a);
-      break;
-    case kEpiQkv:
-      hipLaunchKernelGGL((gemv_kernel<WBF16, NJ, KS, EPI_QKV>), dim3(grid), dim3(kBlock), 0, s, a);
-      break;
-    case kEpiSwiglu:
-      hipLaunchKernelGGL((gemv_kernel<WBF16, NJ, KS, EPI_SWIGLU>), dim3(grid), dim3(kBlock), 0, s, a);
-      break;
-    case kEpiStore2:
-      hipLaunchKernelGGL((gemv_kernel<WBF16, NJ, KS, EPI_STORE2>), dim3(grid), dim3(kBlock), 0, s, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
+  const int groups = (a.ntask + tpw - 1) / tpw;
+  if (groups <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3(gemv_grid(kernel, groups)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
+template <int NJ, int KS>
+static hipError_t go_bf16(int epi, const GemvArgs& a, hipStream_t s) {
+  switch (epi) {
+    case kEpiStore: return go_bf16_epi<NJ, KS, EPI_STORE>(a, s);
+    case kEpiResidual: return go_bf16_epi<NJ, KS, EPI_RESIDUAL>(a, s);
+    case kEpiQkv: return go_bf16_epi<NJ, KS, EPI_QKV>(a, s);
+    case kEpiSwiglu: return go_bf16_epi<NJ, KS, EPI_SWIGLU>(a, s);
+    case kEpiStore2: return go_bf16_epi<NJ, KS, EPI_STORE2>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_gemv_bf16(int epi, const GemvArgs& a, hipStream_t s) {
-  const int ks = gemv_ks(a.cols, 8);
-  const int nj = gemv_nj(a.cols, 8, ks);
+  constexpr int GE = 8;
+  const int ks = gemv_ks(a.cols, GE);
+  const int nj = gemv_nj(a.cols, GE, ks);
   if (ks == 1) {
     if (nj <= 2) return go_bf16<2, 1>(epi, a, s);
     if (nj <= 4) return go_bf16<4, 1>(epi, a, s);
+    if (nj <= 6) return go_bf16<6, 1>(epi, a, s);
     if (nj <= 8) return go_bf16<8, 1>(epi, a, s);
+  }
+  if (ks == 2) {
+    if (nj <= 2) return go_bf16<2, 2>(epi, a, s);
+    if (nj <= 4) return go_bf16<4, 2>(epi, a, s);
+    if (nj <= 6) return go_bf16<6, 2>(epi, a, s);
+    if (nj <= 8) return go_bf16<8, 2>(epi, a, s);
   }
   if (ks == 4) {
     if (nj <= 2) return go_bf16<2, 4>(epi, a, s);
     if (nj <= 4) return go_bf16<4, 4>(epi, a, s);
+    if (nj <= 6) return go_bf16<6, 4>(epi, a, s);
     if (nj <= 8) return go_bf16<8, 4>(epi, a, s);
   }
   return hipErrorInvalidValue;

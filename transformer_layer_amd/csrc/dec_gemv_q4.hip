@@ -3,39 +3,39 @@
 
 namespace dec {
 
-template <int NJ, int KS>
-static hipError_t go_q4(int epi, const GemvArgs& a, hipStream_t s) {
+template <int NJ, int KS, int EPI>
+static hipError_t go_q4_epi(const GemvArgs& a, hipStream_t s) {
+  auto kernel = gemv_kernel<WQ4, NJ, KS, EPI>;
   const int tpw = kWaves / KS;
-  const int grid = (a.ntask + tpw - 1) / tpw;
-  if (grid <= 0) return hipSuccess;
-  switch (epi) {
-    case kEpiStore:
-      hipLaunchKernelGGL((gemv_kernel<WQ4, NJ, KS, EPI_STORE>), dim3(grid), dim3(kBlock), 0, s, a);
-      break;
-    case kEpiResidual:
-      hipLaunchKernelGGL((gemv_kernel<WQ4, NJ, KS, EPI_RESIDUAL>), dim3(grid), dim3(kBlock), 0, s, a);
-      break;
-    case kEpiQkv:
-      hipLaunchKernelGGL((gemv_kernel<WQ4, NJ, KS, EPI_QKV>), dim3(grid), dim3(kBlock), 0, s, a);
-      break;
-    case kEpiSwiglu:
-      hipLaunchKernelGGL((gemv_kernel<WQ4, NJ, KS, EPI_SWIGLU>), dim3(grid), dim3(kBlock), 0, s, a);
-      break;
-    case kEpiStore2:
-      hipLaunchKernelGGL((gemv_kernel<WQ4, NJ, KS, EPI_STORE2>), dim3(grid), dim3(kBlock), 0, s, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
+  const int groups = (a.ntask + tpw - 1) / tpw;
+  if (groups <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3(gemv_grid(kernel, groups)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
+template <int NJ, int KS>
+static hipError_t go_q4(int epi, const GemvArgs& a, hipStream_t s) {
+  switch (epi) {
+    case kEpiStore: return go_q4_epi<NJ, KS, EPI_STORE>(a, s);
+    case kEpiResidual: return go_q4_epi<NJ, KS, EPI_RESIDUAL>(a, s);
+    case kEpiQkv: return go_q4_epi<NJ, KS, EPI_QKV>(a, s);
+    case kEpiSwiglu: return go_q4_epi<NJ, KS, EPI_SWIGLU>(a, s);
+    case kEpiStore2: return go_q4_epi<NJ, KS, EPI_STORE2>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_gemv_q4(int epi, const GemvArgs& a, hipStream_t s) {
-  const int ks = gemv_ks(a.cols, 32);
-  const int nj = gemv_nj(a.cols, 32, ks);
+  constexpr int GE = 32;
+  const int ks = gemv_ks(a.cols, GE);
+  const int nj = gemv_nj(a.cols, GE, ks);
   if (ks == 1) {
     if (nj <= 1) return go_q4<1, 1>(epi, a, s);
     if (nj <= 2) return go_q4<2, 1>(epi, a, s);
+  }
+  if (ks == 2) {
+    if (nj <= 1) return go_q4<1, 2>(epi, a, s);
+    if (nj <= 2) return go_q4<2, 2>(epi, a, s);
   }
   if (ks == 4) {
     if (nj <= 1) return go_q4<1, 4>(epi, a, s);

@@ -35,6 +35,23 @@ struct GemvArgs {
   int null_kernel;
 };
 
+// Granules (16-byte weight groups) per lane for a row of `cols` elements
+// whose columns are split over `ks` waves.
+inline int gemv_nj(int cols, int ge, int ks) {
+  const int G = cols / ge;
+  return (G + 64 * ks - 1) / (64 * ks);
+}
+
+// Waves that share one row (1, 2 or 4): the fewest that keep a lane's slice
+// of the input vector within 32 registers (64 when even four waves cannot).
+// The fused kernels and the per-op RMSNorm both follow this rule, so they
+// accumulate in the same order.
+inline int gemv_ks(int cols, int ge) {
+  for (int ks = 1; ks <= 4; ks *= 2)
+    if (gemv_nj(cols, ge, ks) * ge <= 32) return ks;
+  return 4;
+}
+
 enum GemvEpi { kEpiStore = 0, kEpiResidual = 1, kEpiQkv = 2, kEpiSwiglu = 3, kEpiStore2 = 4 };
 
 // Launch the GEMV core for weight type wtype (0 f32, 1 bf16, 2 q4).

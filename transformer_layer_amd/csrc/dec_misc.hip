@@ -145,8 +145,7 @@ hipError_t launch_rmsnorm_like(const float* x, const void* g, int ntype, float* 
                                float eps, int wtype, int with_weight, int null_kernel,
                                hipStream_t s) {
   const int ge = ge_of(wtype);
-  const int G = n / ge;
-  const int ks = ((G + kWave - 1) / kWave) * ge <= 64 ? 1 : 4;
+  const int ks = gemv_ks(n, ge);
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(kBlock), 0, s, x, g, ntype, out, n, eps, ge, ks,
                      with_weight, null_kernel);
   return hipGetLastError();
