@@ -272,16 +272,20 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   if (threadIdx.x == 0) __hip_atomic_store(&a.counters[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-void attn_plan(int n_kv, int max_ctx, int chunk_req, int* chunk, int* nsplit) {
+void attn_plan(int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit) {
   int c = chunk_req;
   if (c <= 0) {
-    // about two workgroups per compute unit over the whole cache, at most
-    // 64 splits per kv head, chunks a multiple of 16 rows
+    // about two workgroups per compute unit over the whole cache (at most
+    // 64 splits per kv head), chunks a multiple of 16 rows and no longer
+    // than one batch of rows in flight
+    const int lanes_per_row = head_dim * (kvtype == 1 ? 2 : 4) / 16;
+    const int one_batch = (kWave / lanes_per_row) * kWaves * 8;
     int splits = 512 / n_kv;
     if (splits > 64) splits = 64;
     if (splits < 1) splits = 1;
     c = (max_ctx + splits - 1) / splits;
     c = ((c + 15) / 16) * 16;
+    if (c > one_batch) c = one_batch;
   }
   const int cmin = (max_ctx + kSplitMax - 1) / kSplitMax;
   if (c < cmin) c = cmin;

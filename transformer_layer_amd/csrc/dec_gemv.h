@@ -63,27 +63,37 @@ __device__ __forceinline__ float granule_dot<WBF16>(u32x4 w, const float* u, flo
   return acc;
 }
 
+// Byte n of a 32-bit word as a float (v_cvt_f32_ubyte<n>: one instruction,
+// no separate extract).
+__device__ __forceinline__ float ubyte0(uint32_t x) { float r; asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x)); return r; }
+__device__ __forceinline__ float ubyte1(uint32_t x) { float r; asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x)); return r; }
+__device__ __forceinline__ float ubyte2(uint32_t x) { float r; asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x)); return r; }
+__device__ __forceinline__ float ubyte3(uint32_t x) { float r; asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x)); return r; }
+
 // Four-bit granule: returns sum_e (code_e + 8) * u_e. XOR with 0x8 turns each
 // two's-complement nibble into the unsigned value code + 8; the caller
-// subtracts 8 * sum(u) and applies the block scale.
+// subtracts 8 * sum(u) and applies the block scale. Each 32-bit word holds
+// elements 8k..8k+7 (element 2i in the low nibble of byte i); the four words
+// accumulate independently and meet at the end.
 __device__ __forceinline__ float q4_dot_offset(u32x4 w, const float* u) {
-  float s = 0.0f;
   const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  float part[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t t = words[k] ^ 0x88888888u;
     const uint32_t lo = t & 0x0f0f0f0fu;          // elements 8k + 0, 2, 4, 6
     const uint32_t hi = (t >> 4) & 0x0f0f0f0fu;   // elements 8k + 1, 3, 5, 7
-    s = fmaf(float(lo & 0xffu), u[8 * k + 0], s);
-    s = fmaf(float(hi & 0xffu), u[8 * k + 1], s);
-    s = fmaf(float((lo >> 8) & 0xffu), u[8 * k + 2], s);
-    s = fmaf(float((hi >> 8) & 0xffu), u[8 * k + 3], s);
-    s = fmaf(float((lo >> 16) & 0xffu), u[8 * k + 4], s);
-    s = fmaf(float((hi >> 16) & 0xffu), u[8 * k + 5], s);
-    s = fmaf(float(lo >> 24), u[8 * k + 6], s);
-    s = fmaf(float(hi >> 24), u[8 * k + 7], s);
+    float s = ubyte0(lo) * u[8 * k + 0];
+    s = fmaf(ubyte0(hi), u[8 * k + 1], s);
+    s = fmaf(ubyte1(lo), u[8 * k + 2], s);
+    s = fmaf(ubyte1(hi), u[8 * k + 3], s);
+    s = fmaf(ubyte2(lo), u[8 * k + 4], s);
+    s = fmaf(ubyte2(hi), u[8 * k + 5], s);
+    s = fmaf(ubyte3(lo), u[8 * k + 6], s);
+    s = fmaf(ubyte3(hi), u[8 * k + 7], s);
+    part[k] = s;
   }
-  return s;
+  return (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // GE norm-weight values of granule gi (f32 or bf16), with 16-byte loads.
@@ -112,12 +122,17 @@ __device__ __forceinline__ void load_norm_granule(const void* g, int ntype, int 
   }
 }
 
-template <class T, int NJ, int KS, int EPI>
+// One task is NP row pairs (NR = 2 NP rows): a RoPE pair (i, i + d/2) of a
+// head (QKV), a gate row and an up row (gated FFN), or two consecutive rows.
+// PF: the next task's weights are requested before the current task is
+// reduced (more bytes in flight per wave, more registers).
+template <class T, int NJ, int KS, int EPI, int NP, bool PF>
 __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
   constexpr int GE = T::GE;
-  constexpr int NR = 2;  // rows per task
+  constexpr int NR = 2 * NP;  // rows per task
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
   constexpr bool Q4 = (T::ID == 2);
+  constexpr bool PAIRED = (EPI == EPI_SWIGLU || EPI == EPI_STORE2);  // rows from two matrices
   constexpr int TPW = kWaves / KS;  // tasks per workgroup iteration
 
   if (a.null_kernel) return;
@@ -138,40 +153,48 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
   const int G = a.cols / GE;  // granules per row
   const size_t row_bytes = Q4 ? size_t(a.cols) / 2 : size_t(a.cols) * (T::ID == 0 ? 4 : 2);
   const int half = a.d / 2;
+  const int npairs = (EPI == EPI_STORE || EPI == EPI_RESIDUAL) ? (a.rows + 1) / 2 : a.rows / (PAIRED ? 1 : 2);
   const uint8_t* Wa = reinterpret_cast<const uint8_t*>(a.W);
-  const uint8_t* Wb = (EPI == EPI_SWIGLU || EPI == EPI_STORE2) ? reinterpret_cast<const uint8_t*>(a.W2) : Wa;
+  const uint8_t* Wb = PAIRED ? reinterpret_cast<const uint8_t*>(a.W2) : Wa;
   const __half* Sa = reinterpret_cast<const __half*>(a.S);
-  const __half* Sb = (EPI == EPI_SWIGLU || EPI == EPI_STORE2) ? reinterpret_cast<const __half*>(a.S2) : Sa;
+  const __half* Sb = PAIRED ? reinterpret_cast<const __half*>(a.S2) : Sa;
 
-  // the two rows of a task (each from matrix a or b)
-  auto rows_of = [&](int task, int& r0, int& r1) {
+  // rows of pair p: (r0, r1), r0 from matrix a, r1 from matrix a or b
+  auto rows_of = [&](int p, int& r0, int& r1) {
     if constexpr (EPI == EPI_QKV) {
-      r0 = (task / half) * a.d + (task % half);
+      r0 = (p / half) * a.d + (p % half);
       r1 = r0 + half;
-    } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_STORE2) {
-      r0 = task;
-      r1 = task;
+    } else if constexpr (PAIRED) {
+      r0 = p;
+      r1 = p;
     } else {
-      r0 = task * NR;
+      r0 = 2 * p;
       r1 = r0 + 1;
     }
   };
-  // weights (and 4-bit block scales) of a task's rows
+  // weights (and 4-bit block scales) of a task's rows. Loads are never
+  // predicated: a granule past the row end reads the row's last granule
+  // (its input values are zero) and a row past the matrix reads the last row
+  // (its result is never stored).
   auto load_task = [&](int task, u32x4 (&wq)[NR][NJ], float (&sc)[NR][NJ]) {
-    int r0, r1;
-    rows_of(task, r0, r1);
-    const bool v0 = task < a.ntask && r0 < a.rows;
-    const bool v1 = task < a.ntask && r1 < a.rows;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int gi = (j * KS + ks) * kWave + lane;
-      const bool ok = gi < G;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      wq[0][j] = (ok && v0) ? ldg16(Wa + size_t(r0) * row_bytes + size_t(gi) * 16) : z;
-      wq[1][j] = (ok && v1) ? ldg16(Wb + size_t(r1) * row_bytes + size_t(gi) * 16) : z;
-      if constexpr (Q4) {
-        sc[0][j] = (ok && v0) ? __half2float(Sa[size_t(r0) * G + gi]) : 0.0f;
-        sc[1][j] = (ok && v1) ? __half2float(Sb[size_t(r1) * G + gi]) : 0.0f;
+    for (int q = 0; q < NP; ++q) {
+      int p = task * NP + q;
+      p = p < npairs ? p : npairs - 1;
+      int r0, r1;
+      rows_of(p, r0, r1);
+      r0 = r0 < a.rows ? r0 : a.rows - 1;
+      r1 = r1 < a.rows ? r1 : a.rows - 1;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        int gi = (j * KS + ks) * kWave + lane;
+        gi = gi < G ? gi : G - 1;
+        wq[2 * q][j] = ldg16(Wa + size_t(r0) * row_bytes + size_t(gi) * 16);
+        wq[2 * q + 1][j] = ldg16(Wb + size_t(r1) * row_bytes + size_t(gi) * 16);
+        if constexpr (Q4) {
+          sc[2 * q][j] = __half2float(Sa[size_t(r0) * G + gi]);
+          sc[2 * q + 1][j] = __half2float(Sb[size_t(r1) * G + gi]);
+        }
       }
     }
   };
@@ -191,11 +214,12 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
   for (int j = 0; j < NJ; ++j) {
     const int gi = (j * KS + ks) * kWave + lane;
     const bool ok = gi < G;
+    const int gc = ok ? gi : G - 1;
 #pragma unroll
     for (int e = 0; e < GE; e += 4) {
-      float4 v = ok ? *reinterpret_cast<const float4*>(a.in + size_t(gi) * GE + e)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
-      u[j][e] = v.x; u[j][e + 1] = v.y; u[j][e + 2] = v.z; u[j][e + 3] = v.w;
+      const float4 v = *reinterpret_cast<const float4*>(a.in + size_t(gc) * GE + e);
+      u[j][e] = ok ? v.x : 0.0f; u[j][e + 1] = ok ? v.y : 0.0f;
+      u[j][e + 2] = ok ? v.z : 0.0f; u[j][e + 3] = ok ? v.w : 0.0f;
     }
     if constexpr (NORM) {
 #pragma unroll
@@ -203,7 +227,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
     }
   }
   constexpr int kBatch = 16;  // tasks per LDS batch (column-split waves)
-  __shared__ float red[kWaves][kBatch][NR];
+  __shared__ float red[KS > 1 ? kWaves : 1][KS > 1 ? kBatch : 1][NR];
   __shared__ float ssq[kWaves];
   if constexpr (NORM) {
     ss = wave_sum(ss);
@@ -219,14 +243,9 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
     for (int j = 0; j < NJ; ++j) {
       const int gi = (j * KS + ks) * kWave + lane;
       float g[GE];
-      if (gi < G) {
-        load_norm_granule<GE>(a.norm, a.ntype, gi, g);
-      } else {
+      load_norm_granule<GE>(a.norm, a.ntype, gi < G ? gi : G - 1, g);
 #pragma unroll
-        for (int e = 0; e < GE; ++e) g[e] = 0.0f;
-      }
-#pragma unroll
-      for (int e = 0; e < GE; ++e) u[j][e] = (u[j][e] * r) * g[e];
+      for (int e = 0; e < GE; ++e) u[j][e] = (u[j][e] * r) * g[e];   // u is 0 past the row end
     }
   }
   if constexpr (Q4) {
@@ -239,10 +258,11 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
     }
   }
 
-  // ---- epilogue of one task (run by one lane)
-  auto epilogue = [&](int task, float y0, float y1) {
+  // ---- epilogue of one row pair (run by one lane)
+  auto epilogue = [&](int p, float y0, float y1) {
+    if (p >= npairs) return;
     int r0, r1;
-    rows_of(task, r0, r1);
+    rows_of(p, r0, r1);
     const bool v0 = r0 < a.rows;
     const bool v1 = r1 < a.rows;
     if constexpr (EPI == EPI_STORE) {
@@ -257,8 +277,8 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
       a.y[r0] = y0;
       a.y2[r0] = y1;
     } else {  // EPI_QKV
-      const int head = task / half;
-      const int i = task % half;
+      const int head = p / half;
+      const int i = p % half;
       if (head < a.nq + a.nkv) {
         const float c = a.rope[(size_t(pos) * half + i) * 2];
         const float s = a.rope[(size_t(pos) * half + i) * 2 + 1];
@@ -285,59 +305,83 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
     }
   };
 
-  // ---- tasks: this wave slot handles task, task + stride, ...; the next
-  // task's weights are in flight while the current one is reduced
-  int nb = 0;                                // tasks in the current LDS batch
-  int batch_base = blockIdx.x * TPW;         // base of its first task
+  // ---- tasks: this wave slot handles task, task + stride, ...
+  int nb = 0;                         // tasks in the current LDS batch
+  int batch_base = blockIdx.x * TPW;  // base of its first task
   for (int base = blockIdx.x * TPW; base < a.ntask; base += stride) {
     const int task = base + slot;
-    const bool tvalid = task < a.ntask;
-
-    u32x4 wn[NR][NJ];
-    float sn[NR][NJ];
     const bool more = base + stride < a.ntask;
-    if (more) load_task(task + stride, wn, sn);
+    u32x4 wn[PF ? NR : 1][NJ];
+    float sn[PF ? NR : 1][NJ];
+    if constexpr (PF) {
+      if (more) load_task(task + stride, wn, sn);
+    }
 
-    float acc[NR] = {0.0f, 0.0f};
+    float acc[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) acc[k] = 0.0f;
     if constexpr (Q4) {
 #pragma unroll
       for (int k = 0; k < NR; ++k)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int j = 0; j < NJ; ++j) {
           acc[k] = fmaf(sc[k][j], q4_dot_offset(wq[k][j], u[j]) - usum[j], acc[k]);
+          // keep each granule's conversions next to its multiply-adds (the
+          // scheduler would otherwise convert every granule first and run
+          // out of registers)
+          __builtin_amdgcn_sched_barrier(0);
+        }
     } else {
 #pragma unroll
       for (int k = 0; k < NR; ++k)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[k] = granule_dot<T>(wq[k][j], u[j], acc[k]);
     }
-    if (more) {
+    if constexpr (PF) {
+      if (more) {
 #pragma unroll
-      for (int k = 0; k < NR; ++k)
+        for (int k = 0; k < NR; ++k)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          wq[k][j] = wn[k][j];
-          if constexpr (Q4) sc[k][j] = sn[k][j];
-        }
+          for (int j = 0; j < NJ; ++j) {
+            wq[k][j] = wn[k][j];
+            if constexpr (Q4) sc[k][j] = sn[k][j];
+          }
+      }
+    } else {
+      if (more) load_task(task + stride, wq, sc);
     }
 #pragma unroll
     for (int k = 0; k < NR; ++k) acc[k] = wave_sum(acc[k]);
     if constexpr (KS == 1) {
-      if (lane == 0 && tvalid) epilogue(task, acc[0], acc[1]);
+      if (lane < NP) {
+        // lane q finishes pair q of the task
+        float y0 = acc[0], y1 = acc[1];
+#pragma unroll
+        for (int q = 1; q < NP; ++q)
+          if (lane == q) { y0 = acc[2 * q]; y1 = acc[2 * q + 1]; }
+        epilogue(task * NP + lane, y0, y1);
+      }
     } else {
       // partial sums of the KS waves meet in LDS; finished in batches so the
       // waves do not meet at a barrier for every task
-      if (lane == 0) { red[wv][nb][0] = acc[0]; red[wv][nb][1] = acc[1]; }
+      if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) red[wv][nb][k] = acc[k];
+      }
       ++nb;
-      if (nb == kBatch || base + stride >= a.ntask) {
+      if (nb == kBatch || !more) {
         __syncthreads();
-        if (ks == 0 && lane < nb) {
-          const int t = batch_base + lane * stride + slot;
-          if (t < a.ntask) {
+        if (ks == 0) {
+          for (int e = lane; e < nb * NP; e += kWave) {
+            const int bi = e / NP, q = e % NP;
+            const int t = batch_base + bi * stride + slot;
             float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-            for (int k = 0; k < KS; ++k) { s0 += red[slot * KS + k][lane][0]; s1 += red[slot * KS + k][lane][1]; }
-            epilogue(t, s0, s1);
+            for (int k = 0; k < KS; ++k) {
+              s0 += red[slot * KS + k][bi][2 * q];
+              s1 += red[slot * KS + k][bi][2 * q + 1];
+            }
+            if (t < a.ntask) epilogue(t * NP + q, s0, s1);
           }
         }
         __syncthreads();

@@ -3,9 +3,16 @@
 
 namespace dec {
 
+// Row pairs per task: enough that a wave keeps at least eight 16-byte
+// weight loads in flight (NJ granules per row, two rows per pair).
+template <int NJ>
+constexpr int pairs_per_task() { return NJ >= 4 ? 1 : (NJ >= 2 ? 2 : 4); }
+
 template <int NJ, int KS, int EPI>
-static hipError_t go_bf16_epi(const GemvArgs& a, hipStream_t s) {
-  auto kernel = gemv_kernel<WBF16, NJ, KS, EPI>;
+static hipError_t go_bf16_epi(GemvArgs a, hipStream_t s) {
+  constexpr int NP = pairs_per_task<NJ>();
+  auto kernel = gemv_kernel<WBF16, NJ, KS, EPI, NP, true>;
+  a.ntask = (a.ntask + NP - 1) / NP;  // row pairs -> tasks
   const int tpw = kWaves / KS;
   const int groups = (a.ntask + tpw - 1) / tpw;
   if (groups <= 0) return hipSuccess;

@@ -3,9 +3,18 @@
 
 namespace dec {
 
+// Row pairs per task. A 4-bit granule costs about 80 vector instructions
+// for 16 bytes, so these kernels are limited by instruction issue rather
+// than by loads in flight: one pair per task keeps registers low and
+// occupancy high.
+template <int NJ>
+constexpr int pairs_per_task() { return 1; }
+
 template <int NJ, int KS, int EPI>
-static hipError_t go_q4_epi(const GemvArgs& a, hipStream_t s) {
-  auto kernel = gemv_kernel<WQ4, NJ, KS, EPI>;
+static hipError_t go_q4_epi(GemvArgs a, hipStream_t s) {
+  constexpr int NP = pairs_per_task<NJ>();
+  auto kernel = gemv_kernel<WQ4, NJ, KS, EPI, NP, true>;
+  a.ntask = (a.ntask + NP - 1) / NP;  // row pairs -> tasks
   const int tpw = kWaves / KS;
   const int groups = (a.ntask + tpw - 1) / tpw;
   if (groups <= 0) return hipSuccess;

@@ -17,7 +17,7 @@ struct GemvArgs {
   const void* S2;
   int rows;            // rows of the matrix / matrices
   int cols;            // input length
-  int ntask;           // tasks (two rows each)
+  int ntask;           // row pairs (the launcher turns them into tasks)
   const float* in;     // input vector [cols]
   const void* norm;    // RMSNorm weight [cols] (norm prologue only)
   int ntype;           // 0 f32, 1 bf16
@@ -73,7 +73,7 @@ struct AttnArgs {
 };
 
 // attention chunk (positions per split) and split count for a shape
-void attn_plan(int n_kv, int max_ctx, int chunk_req, int* chunk, int* nsplit);
+void attn_plan(int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
 // small per-op and per-token kernels
