@@ -3,15 +3,17 @@
 
 namespace dec {
 
-// Row pairs per task: enough that a wave keeps at least eight 16-byte
-// weight loads in flight (NJ granules per row, two rows per pair).
+// Row pairs per task: two when a lane holds few granules of a row, so that a
+// wave still has several 16-byte loads in flight; one otherwise (fewer
+// registers, higher occupancy). Measured on the 7B/9B layer shapes, fetching
+// the next task ahead (PF) did not help once occupancy was high.
 template <int NJ>
-constexpr int pairs_per_task() { return NJ >= 4 ? 1 : (NJ >= 2 ? 2 : 4); }
+constexpr int pairs_per_task() { return NJ <= 2 ? 2 : 1; }
 
 template <int NJ, int KS, int EPI>
 static hipError_t go_bf16_epi(GemvArgs a, hipStream_t s) {
   constexpr int NP = pairs_per_task<NJ>();
-  auto kernel = gemv_kernel<WBF16, NJ, KS, EPI, NP, true>;
+  auto kernel = gemv_kernel<WBF16, NJ, KS, EPI, NP, false>;
   a.ntask = (a.ntask + NP - 1) / NP;  // row pairs -> tasks
   const int tpw = kWaves / KS;
   const int groups = (a.ntask + tpw - 1) / tpw;

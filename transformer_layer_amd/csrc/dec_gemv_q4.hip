@@ -3,17 +3,17 @@
 
 namespace dec {
 
-// Row pairs per task. A 4-bit granule costs about 80 vector instructions
-// for 16 bytes, so these kernels are limited by instruction issue rather
-// than by loads in flight: one pair per task keeps registers low and
-// occupancy high.
+// Row pairs per task: two when a lane holds few granules of a row, so that a
+// wave still has several 16-byte loads in flight; one otherwise (fewer
+// registers, higher occupancy). Measured on the 7B/9B layer shapes, fetching
+// the next task ahead (PF) did not help once occupancy was high.
 template <int NJ>
-constexpr int pairs_per_task() { return 1; }
+constexpr int pairs_per_task() { return NJ <= 1 ? 2 : 1; }
 
 template <int NJ, int KS, int EPI>
 static hipError_t go_q4_epi(GemvArgs a, hipStream_t s) {
   constexpr int NP = pairs_per_task<NJ>();
-  auto kernel = gemv_kernel<WQ4, NJ, KS, EPI, NP, true>;
+  auto kernel = gemv_kernel<WQ4, NJ, KS, EPI, NP, false>;
   a.ntask = (a.ntask + NP - 1) / NP;  // row pairs -> tasks
   const int tpw = kWaves / KS;
   const int groups = (a.ntask + tpw - 1) / tpw;

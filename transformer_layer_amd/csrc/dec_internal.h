@@ -43,12 +43,14 @@ inline int gemv_nj(int cols, int ge, int ks) {
 }
 
 // Waves that share one row (1, 2 or 4): the fewest that keep a lane's slice
-// of the input vector within 32 registers (64 when even four waves cannot).
+// of the input vector within `budget` registers (16 for f32/bf16 weights, 32
+// for 4-bit weights, whose granules hold 32 elements); four when none does.
 // The fused kernels and the per-op RMSNorm both follow this rule, so they
 // accumulate in the same order.
 inline int gemv_ks(int cols, int ge) {
+  const int budget = ge == 32 ? 32 : 16;
   for (int ks = 1; ks <= 4; ks *= 2)
-    if (gemv_nj(cols, ge, ks) * ge <= 32) return ks;
+    if (gemv_nj(cols, ge, ks) * ge <= budget) return ks;
   return 4;
 }
 
