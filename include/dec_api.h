@@ -190,6 +190,19 @@ int dec_gated_ffn(const dec_layer_desc* desc, const void* ffn_norm, dec_mat wgat
 int dec_layer_step(const dec_layer_desc* desc, const dec_layer_weights* w,
                    const dec_layer_state* st, void* stream);
 
+/* ---- LM head ------------------------------------------------------------- */
+
+/* Final RMSNorm, LM head and greedy choice of the next token: the "LM head +
+   sampling" segment of the per-token budget in "RDNA4 Decode Kernel Fusion:
+   Pipeline Barriers, Not Launches, Are the Win" (section "What it does to
+   the token"); sampling is greedy. u = x / sqrt(mean(x^2) + eps) * final_norm
+   (norm weight in desc->ntype), logits = W_head u with W_head [vocab][H] in
+   head_type (DEC_F32 | DEC_BF16 | DEC_Q4), *token = argmax logits (the lowest
+   index among equal maxima). Writes logits (float32 [vocab]) and *token.
+   Two kernels: the GEMV with the norm prologue, and a one-workgroup argmax. */
+int dec_lm_head(const dec_layer_desc* desc, int32_t head_type, const void* final_norm, dec_mat head,
+                int32_t vocab, const float* x, float* logits, int32_t* token, void* stream);
+
 /* ---- per-token bookkeeping --------------------------------------------- */
 
 /* RoPE table: table[p][i] = (cos(p w_i), sin(p w_i)), w_i = theta^(-2i/d),

@@ -41,6 +41,12 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64, copy=False)
 
 
+# two's-complement value of each 4-bit pattern 0..15
+_Q4_SIGNED = np.array([0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5, -4, -3, -2, -1], dtype=np.float64)
+# for every byte value b: (value of the low nibble, value of the high nibble)
+_Q4_PAIRS = np.stack([_Q4_SIGNED[np.arange(256) & 0x0F], _Q4_SIGNED[np.arange(256) >> 4]], axis=1)
+
+
 def q4_dequant(nib: np.ndarray, scales: np.ndarray, dtype=np.float64) -> np.ndarray:
     """4-bit block weights to real values: w[r, c] = scale[r, c // 32] * code[r, c].
 
@@ -51,11 +57,7 @@ def q4_dequant(nib: np.ndarray, scales: np.ndarray, dtype=np.float64) -> np.ndar
     """
     rows, half = nib.shape
     cols = half * 2
-    # two's-complement value of each 4-bit pattern 0..15
-    signed = np.array([0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5, -4, -3, -2, -1], dtype=np.float64)
-    codes = np.empty((rows, half, 2), dtype=np.float64)
-    codes[:, :, 0] = signed[nib & 0x0F]      # element 2i: low nibble of byte i
-    codes[:, :, 1] = signed[nib >> 4]        # element 2i+1: high nibble
+    codes = _Q4_PAIRS[nib].reshape(rows, cols)   # [rows, half, 2] -> element order 2i, 2i+1
     s = scales.astype(np.float64)
     w = codes.reshape(rows, cols // 32, 32) * s[:, :, None]
     return w.reshape(rows, cols).astype(dtype, copy=False)
@@ -203,8 +205,12 @@ class Oracle:
         self._deq = {}
         cdt = np.float32 if cfg.kvtype == "f32" else np.uint16
         shape = (cfg.n_kv_heads, cfg.max_ctx, cfg.head_dim)
+        # the cache in its storage encoding, and the same entries decoded to
+        # real values (written together; attention reads the decoded copy)
         self.K = [np.zeros(shape, dtype=cdt) for _ in layers]
         self.V = [np.zeros(shape, dtype=cdt) for _ in layers]
+        self.Kd = [np.zeros(shape, dtype=self.dtype) for _ in layers]
+        self.Vd = [np.zeros(shape, dtype=self.dtype) for _ in layers]
 
     # -- weights
     ROWS_PER_SLICE = 128
@@ -247,6 +253,8 @@ class Oracle:
         n = K.data.shape[1]
         self.K[l][:, :n] = K.data
         self.V[l][:, :n] = V.data
+        self.Kd[l][:, :n] = cache_values(self.K[l][:, :n], self.cfg.kvtype, self.dtype)
+        self.Vd[l][:, :n] = cache_values(self.V[l][:, :n], self.cfg.kvtype, self.dtype)
 
     # -- the layer's steps, in the order of [P1]
     def qkv_rope_append(self, l: int, x: np.ndarray, p: int) -> np.ndarray:
@@ -263,15 +271,14 @@ class Oracle:
         k = rope(k, p, c.rope_theta)
         self.K[l][:, p, :] = round_to_cache(k, c.kvtype)
         self.V[l][:, p, :] = round_to_cache(v, c.kvtype)
+        self.Kd[l][:, p, :] = cache_values(self.K[l][:, p, :], c.kvtype, self.dtype)
+        self.Vd[l][:, p, :] = cache_values(self.V[l][:, p, :], c.kvtype, self.dtype)
         return q
 
     def attention(self, l: int, q: np.ndarray, p: int) -> np.ndarray:
         """Attention of q over cache positions 0..p of layer l; returns the
         head outputs concatenated in head order, ``[n_q * d]``."""
-        c = self.cfg
-        K = cache_values(self.K[l][:, : p + 1], c.kvtype, self.dtype)
-        V = cache_values(self.V[l][:, : p + 1], c.kvtype, self.dtype)
-        return attend(q, K, V, c.group).reshape(-1)
+        return attend(q, self.Kd[l][:, : p + 1], self.Vd[l][:, : p + 1], self.cfg.group).reshape(-1)
 
     def ffn(self, l: int, x: np.ndarray) -> np.ndarray:
         """Post-attention RMSNorm, gate and up projections, SwiGLU: h ``[F]``."""

@@ -304,6 +304,31 @@ int dec_layer_step(const dec_layer_desc* d, const dec_layer_weights* w, const de
   return residual_launch(d, w->wdown, H, F, st->h, st->x, s);
 }
 
+int dec_lm_head(const dec_layer_desc* d, int32_t head_type, const void* final_norm, dec_mat head,
+                int32_t vocab, const float* x, float* logits, int32_t* token, void* stream) {
+  int rc;
+  if ((rc = check_desc(d))) return rc;
+  if (head_type < DEC_F32 || head_type > DEC_Q4) return fail(DEC_E_DTYPE, "head_type %d", head_type);
+  if (!final_norm || !x || !logits || !token) return fail(DEC_E_NULL, "final_norm/x/logits/token is NULL");
+  if (!head.w) return fail(DEC_E_NULL, "head is NULL");
+  if (!aligned16(head.w) || !aligned16(x)) return fail(DEC_E_ALIGN, "head/x not 16-byte aligned");
+  if (head_type == DEC_Q4 && !head.scales) return fail(DEC_E_NULL, "head scales are NULL");
+  if (vocab <= 0) return fail(DEC_E_SHAPE, "vocab %d", vocab);
+  if (d->hidden % ge_of(head_type)) return fail(DEC_E_SHAPE, "hidden %d vs head type", d->hidden);
+  hipStream_t s = hipStream_t(stream);
+  dec::GemvArgs a = base_args(d);
+  a.W = head.w;
+  a.S = head.scales;
+  a.rows = vocab;
+  a.cols = d->hidden;
+  a.ntask = (vocab + 1) / 2;
+  a.in = x;
+  a.norm = final_norm;
+  a.y = logits;
+  if ((rc = launched(gemv(head_type, dec::kEpiNormStore, a, s), "lm_head"))) return rc;
+  return launched(dec::launch_argmax(logits, vocab, token, s), "argmax");
+}
+
 int dec_rope_table(double theta, int32_t head_dim, int32_t max_ctx, float* table, void* stream) {
   if (!table) return fail(DEC_E_NULL, "table is NULL");
   if (!(theta > 0.0) || head_dim <= 0 || head_dim % 2 || max_ctx <= 0)

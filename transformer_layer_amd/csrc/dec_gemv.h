@@ -18,6 +18,7 @@
 //                 appended to the cache at position *pos    (QKV projection)
 //   EPI_SWIGLU    h[j] = silu(Wg[j] u) * (Wu[j] u)             (gated FFN)
 //   EPI_STORE2    y[j] = Wg[j] u, y2[j] = Wu[j] u              (per-op gate/up)
+//   EPI_NORM_STORE  y[r] = W norm(x) (final RMSNorm + LM head logits)
 #pragma once
 
 #include "dec_device.h"
@@ -31,7 +32,7 @@ struct WF32 { static constexpr int GE = 4; static constexpr int ID = 0; };
 struct WBF16 { static constexpr int GE = 8; static constexpr int ID = 1; };
 struct WQ4 { static constexpr int GE = 32; static constexpr int ID = 2; };
 
-enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_STORE2 = 4 };
+enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_STORE2 = 4, EPI_NORM_STORE = 5 };
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -130,7 +131,7 @@ template <class T, int NJ, int KS, int EPI, int NP, bool PF>
 __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
   constexpr int GE = T::GE;
   constexpr int NR = 2 * NP;  // rows per task
-  constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
+  constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_NORM_STORE);
   constexpr bool Q4 = (T::ID == 2);
   constexpr bool PAIRED = (EPI == EPI_SWIGLU || EPI == EPI_STORE2);  // rows from two matrices
   constexpr int TPW = kWaves / KS;  // tasks per workgroup iteration
@@ -153,7 +154,8 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
   const int G = a.cols / GE;  // granules per row
   const size_t row_bytes = Q4 ? size_t(a.cols) / 2 : size_t(a.cols) * (T::ID == 0 ? 4 : 2);
   const int half = a.d / 2;
-  const int npairs = (EPI == EPI_STORE || EPI == EPI_RESIDUAL) ? (a.rows + 1) / 2 : a.rows / (PAIRED ? 1 : 2);
+  constexpr bool CONSEC = (EPI == EPI_STORE || EPI == EPI_RESIDUAL || EPI == EPI_NORM_STORE);  // consecutive rows
+  const int npairs = CONSEC ? (a.rows + 1) / 2 : a.rows / (PAIRED ? 1 : 2);
   const uint8_t* Wa = reinterpret_cast<const uint8_t*>(a.W);
   const uint8_t* Wb = PAIRED ? reinterpret_cast<const uint8_t*>(a.W2) : Wa;
   const __half* Sa = reinterpret_cast<const __half*>(a.S);
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
     rows_of(p, r0, r1);
     const bool v0 = r0 < a.rows;
     const bool v1 = r1 < a.rows;
-    if constexpr (EPI == EPI_STORE) {
+    if constexpr (EPI == EPI_STORE || EPI == EPI_NORM_STORE) {
       if (v0) a.y[r0] = y0;
       if (v1) a.y[r1] = y1;
     } else if constexpr (EPI == EPI_RESIDUAL) {

@@ -30,6 +30,7 @@ static hipError_t go_f32(int epi, const GemvArgs& a, hipStream_t s) {
     case kEpiQkv: return go_f32_epi<NJ, KS, EPI_QKV>(a, s);
     case kEpiSwiglu: return go_f32_epi<NJ, KS, EPI_SWIGLU>(a, s);
     case kEpiStore2: return go_f32_epi<NJ, KS, EPI_STORE2>(a, s);
+    case kEpiNormStore: return go_f32_epi<NJ, KS, EPI_NORM_STORE>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

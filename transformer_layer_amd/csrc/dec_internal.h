@@ -54,7 +54,7 @@ inline int gemv_ks(int cols, int ge) {
   return 4;
 }
 
-enum GemvEpi { kEpiStore = 0, kEpiResidual = 1, kEpiQkv = 2, kEpiSwiglu = 3, kEpiStore2 = 4 };
+enum GemvEpi { kEpiStore = 0, kEpiResidual = 1, kEpiQkv = 2, kEpiSwiglu = 3, kEpiStore2 = 4, kEpiNormStore = 5 };
 
 // Launch the GEMV core for weight type wtype (0 f32, 1 bf16, 2 q4).
 hipError_t launch_gemv_f32(int epi, const GemvArgs& a, hipStream_t s);
@@ -93,6 +93,7 @@ hipError_t launch_swiglu(const float* g, const float* u, float* h, int n, int nu
 hipError_t launch_rope_table(double theta, int d, int max_ctx, float* table, hipStream_t s);
 hipError_t launch_embed(const float* embed, int vocab, int hidden, const int32_t* token, float* x,
                         uint32_t* err, hipStream_t s);
+hipError_t launch_argmax(const float* v, int n, int32_t* out, hipStream_t s);
 hipError_t launch_advance(int32_t* pos, int pos_lo, int pos_hi, const int32_t* tokens,
                           int32_t* token, hipStream_t s);
 

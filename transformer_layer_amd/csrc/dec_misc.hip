@@ -139,6 +139,38 @@ __global__ void advance_kernel(int32_t* pos, int pos_lo, int pos_hi, const int32
   if (tokens) *token = tokens[p - pos_lo];
 }
 
+// Index of the largest value (the lowest index among equal maxima), one
+// workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void argmax_kernel(const float* v, int n, int32_t* out) {
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const float x = v[i];
+    if (x > best || (x == best && i < bi)) { best = x; bi = i; }
+  }
+  // wave reduction, then across the 16 waves in LDS
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ob = __shfl_xor(best, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+  }
+  __shared__ float sb[16];
+  __shared__ int si[16];
+  const int wv = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) { sb[wv] = best; si[wv] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < int(blockDim.x / kWave); ++w)
+      if (sb[w] > best || (sb[w] == best && si[w] < bi)) { best = sb[w]; bi = si[w]; }
+    *out = bi;
+  }
+}
+
+hipError_t launch_argmax(const float* v, int n, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(argmax_kernel, dim3(1), dim3(1024), 0, s, v, n, out);
+  return hipGetLastError();
+}
+
 static int ge_of(int wtype) { return wtype == 0 ? 4 : wtype == 1 ? 8 : 32; }
 
 hipError_t launch_rmsnorm_like(const float* x, const void* g, int ntype, float* out, int n,

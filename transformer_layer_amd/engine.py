@@ -77,6 +77,8 @@ class DecodeStack:
         self.state = [self._state(l) for l in range(self.n_layers)]
         self.embed = None
         self.tokens_dev = None
+        self.head = None
+        self.logits = None
 
     def _state(self, l: int) -> L.dec_layer_state:
         p = L.ptr
@@ -102,6 +104,13 @@ class DecodeStack:
     def set_embedding(self, embed) -> None:
         self.embed = _upload(embed, self.dev)[0]
 
+    def set_head(self, final_norm, head) -> None:
+        """Final norm weight and LM head [vocab, H] (storage encoding)."""
+        self.final_norm = _upload(final_norm, self.dev)[0]
+        self.head = _upload(head, self.dev)
+        self.head_type = L.DTYPES[head.kind]
+        self.logits = torch.zeros(self.cfg.vocab, dtype=torch.float32, device=self.dev)
+
     def set_pos(self, p: int) -> None:
         self.pos.fill_(int(p))
 
@@ -120,14 +129,19 @@ class DecodeStack:
         L.dec_embed(self.embed.data_ptr(), c.vocab, c.hidden, self.token.data_ptr(), self.x.data_ptr(),
                     self.err.data_ptr(), stream)
 
-    def advance(self, pos_lo: int, pos_hi: int, stream=None) -> None:
-        L.dec_advance(self.pos.data_ptr(), pos_lo, pos_hi, L.ptr(self.tokens_dev), self.token.data_ptr(),
-                      stream)
+    def advance(self, pos_lo: int, pos_hi: int, stream=None, use_list=True) -> None:
+        toks = L.ptr(self.tokens_dev) if use_list else None
+        L.dec_advance(self.pos.data_ptr(), pos_lo, pos_hi, toks, self.token.data_ptr(), stream)
 
-    def token_step(self, pos_lo=None, pos_hi=None, record=None, stream=None) -> None:
-        """One token: embed, every layer, advance. With `record` (a
-        [n_layers+1, H] float tensor) x is copied after the embedding and
-        after every layer."""
+    def head_step(self, stream=None) -> None:
+        """Final norm, LM head and greedy argmax: writes the next token."""
+        L.dec_lm_head(self.desc, self.head_type, self.final_norm.data_ptr(), _mat(self.head), self.cfg.vocab,
+                      self.x.data_ptr(), self.logits.data_ptr(), self.token.data_ptr(), stream)
+
+    def token_step(self, pos_lo=None, pos_hi=None, record=None, stream=None, greedy=False) -> None:
+        """One token: embed, every layer, (greedy: LM head and argmax into
+        the token), advance. With `record` (a [n_layers+1, H] float tensor) x
+        is copied after the embedding and after every layer."""
         self.embed_token(stream)
         if record is not None:
             record[0].copy_(self.x)
@@ -135,15 +149,17 @@ class DecodeStack:
             self.layer(l, stream)
             if record is not None:
                 record[l + 1].copy_(self.x)
+        if greedy:
+            self.head_step(stream)
         if pos_lo is not None:
-            self.advance(pos_lo, pos_hi, stream)
+            self.advance(pos_lo, pos_hi, stream, use_list=not greedy)
 
-    def capture(self, pos_lo: int, pos_hi: int) -> torch.cuda.CUDAGraph:
-        """Record one token (embed, layers, advance) into a HIP graph."""
+    def capture(self, pos_lo: int, pos_hi: int, greedy: bool = False) -> torch.cuda.CUDAGraph:
+        """Record one token (embed, layers, [head], advance) into a HIP graph."""
         g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            self.token_step(pos_lo, pos_hi)
+            self.token_step(pos_lo, pos_hi, greedy=greedy)
         return g
 
     def check_err(self) -> int:

@@ -60,6 +60,8 @@ SIGNATURES = {
     "dec_gemv_residual": (ctypes.c_int, [P_DESC, dec_mat, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "dec_gated_ffn": (ctypes.c_int, [P_DESC, c_void_p, dec_mat, dec_mat, c_void_p, c_void_p, c_void_p]),
     "dec_layer_step": (ctypes.c_int, [P_DESC, P_W, P_ST, c_void_p]),
+    "dec_lm_head": (ctypes.c_int, [P_DESC, c_int32, c_void_p, dec_mat, c_int32, c_void_p, c_void_p, c_void_p,
+                                    c_void_p]),
     "dec_rope_table": (ctypes.c_int, [c_double, c_int32, c_int32, c_void_p, c_void_p]),
     "dec_embed": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dec_advance": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
@@ -148,6 +150,12 @@ def dec_gated_ffn(desc, ffn_norm: int, wgate: dec_mat, wup: dec_mat, x: int, h: 
 def dec_layer_step(desc, weights, state, stream=None) -> None:
     _check(load().dec_layer_step(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(state),
                                  _s(stream)), "dec_layer_step")
+
+
+def dec_lm_head(desc, head_type: int, final_norm: int, head: dec_mat, vocab: int, x: int, logits: int,
+                token: int, stream=None) -> None:
+    _check(load().dec_lm_head(ctypes.byref(desc), head_type, final_norm, head, vocab, x, logits, token,
+                              _s(stream)), "dec_lm_head")
 
 
 def dec_rope_table(theta: float, head_dim: int, max_ctx: int, table: int, stream=None) -> None:
