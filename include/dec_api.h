@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define DEC_ABI_VERSION 1
+#define DEC_ABI_VERSION 2
 
 enum dec_dtype { DEC_F32 = 0, DEC_BF16 = 1, DEC_Q4 = 2 };
 
@@ -67,6 +67,10 @@ enum dec_status {
   DEC_E_LAUNCH = -5,      /* the HIP runtime rejected a launch */
   DEC_E_UNSUPPORTED = -6  /* valid request this build does not implement */
 };
+
+/* uint32 words per kv head in dec_layer_state.counters: each head's arrival
+   counter is word j * DEC_COUNTER_STRIDE, alone on its 64-byte line */
+#define DEC_COUNTER_STRIDE 16
 
 /* bits of the device error word */
 #define DEC_ERR_POS 0x1u
@@ -120,9 +124,10 @@ typedef struct {
   float* q;            /* [n_q d] rotated queries (written by the QKV kernel) */
   float* attn;         /* [n_q d] attention output, heads in order */
   float* h;            /* [F] SwiGLU output, input of the down projection */
-  float* part;         /* [dec_attn_part_floats(desc)] split partials */
-  uint32_t* counters;  /* [n_kv] arrival counters; zero before first use, and
-                          the attention kernel leaves them zero */
+  float* part;         /* [dec_attn_part_floats(desc)] split partials, 16-byte aligned */
+  uint32_t* counters;  /* [n_kv * DEC_COUNTER_STRIDE] arrival counters; zero
+                          before first use, and the attention kernel leaves
+                          them zero */
   void* k_cache;       /* this layer's keys   [n_kv][max_ctx][d] in kvtype */
   void* v_cache;       /* this layer's values [n_kv][max_ctx][d] in kvtype */
   const int32_t* pos;  /* position p of the token being decoded */

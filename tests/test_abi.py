@@ -85,6 +85,7 @@ int main(void) {
   printf("DEC_F32 value %d\nDEC_BF16 value %d\nDEC_Q4 value %d\n", DEC_F32, DEC_BF16, DEC_Q4);
   printf("DEC_UNFUSED value %u\nDEC_NULL_KERNELS value %u\n", DEC_UNFUSED, DEC_NULL_KERNELS);
   printf("DEC_ERR_POS value %u\nDEC_ERR_TOKEN value %u\n", DEC_ERR_POS, DEC_ERR_TOKEN);
+  printf("DEC_COUNTER_STRIDE value %d\n", DEC_COUNTER_STRIDE);
   printf("DEC_E_NULL value %d\nDEC_E_SHAPE value %d\nDEC_E_DTYPE value %d\nDEC_E_ALIGN value %d\n",
          DEC_E_NULL, DEC_E_SHAPE, DEC_E_DTYPE, DEC_E_ALIGN);
   return 0;
@@ -109,14 +110,14 @@ def test_struct_layout_matches_a_c_compiler(L, tmp_path):
                     "DEC_UNFUSED": L.DEC_UNFUSED, "DEC_NULL_KERNELS": L.DEC_NULL_KERNELS,
                     "DEC_ERR_POS": L.DEC_ERR_POS, "DEC_ERR_TOKEN": L.DEC_ERR_TOKEN,
                     "DEC_E_NULL": E_NULL, "DEC_E_SHAPE": E_SHAPE, "DEC_E_DTYPE": E_DTYPE,
-                    "DEC_E_ALIGN": E_ALIGN}[name]
+                    "DEC_E_ALIGN": E_ALIGN, "DEC_COUNTER_STRIDE": L.DEC_COUNTER_STRIDE}[name]
             assert val == want, name
         elif field == "size":
             assert ctypes.sizeof(getattr(L, name)) == val, name
         else:
             assert getattr(getattr(L, name), field).offset == val, f"{name}.{field}"
         seen += 1
-    assert seen == 48   # 4 sizes, 33 offsets, 11 constants
+    assert seen == 49   # 4 sizes, 33 offsets, 12 constants
 
 
 # ---- host-side checks (every call below is rejected before any launch)

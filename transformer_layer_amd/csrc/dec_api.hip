@@ -158,7 +158,8 @@ int check_state(const dec_layer_state* st, bool scratch) {
     return fail(DEC_E_NULL, "a state pointer is NULL");
   if (scratch && !st->scratch) return fail(DEC_E_NULL, "scratch is NULL (needed by DEC_UNFUSED)");
   for (const void* p : {(const void*)st->x, (const void*)st->q, (const void*)st->attn,
-                        (const void*)st->h, (const void*)st->k_cache, (const void*)st->v_cache})
+                        (const void*)st->h, (const void*)st->part, (const void*)st->k_cache,
+                        (const void*)st->v_cache})
     if (!aligned16(p)) return fail(DEC_E_ALIGN, "state buffer not 16-byte aligned");
   if (scratch && !aligned16(st->scratch)) return fail(DEC_E_ALIGN, "scratch not 16-byte aligned");
   return DEC_OK;

@@ -10,11 +10,15 @@
 // of V rows is requested together with K.
 //
 // The last workgroup of a kv head to arrive combines the partials with a
-// log-sum-exp rescale. Ordering: every lane waits for its own partial stores
-// to complete, the workgroup meets at a barrier, and one thread performs an
-// agent-scope acquire-release increment of the head's counter; the last
-// arriver acquires at agent scope before reading. The combiner resets the
-// counter, so the kernel replays unchanged inside a graph.
+// log-sum-exp rescale. Ordering without an L2 write-back: the partials are
+// written with agent-scope atomic stores, which reach the device-coherent
+// level by themselves; every lane waits until its stores have completed
+// (vmcnt 0), the workgroup meets at a barrier, and one thread increments the
+// head's counter with an agent-scope atomic. Every counter sits on its own
+// 64-byte line, so the heads' arrivals do not queue on one line. The last
+// arriver's agent-scope acquire fence drops stale cached lines before it
+// reads the partials. The combiner resets the counter, so the kernel replays
+// unchanged inside a graph.
 #include "dec_device.h"
 #include "dec_internal.h"
 
@@ -35,6 +39,12 @@ __device__ __forceinline__ void unpack_row(u32x4 v, float* f) {
     f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
   }
+}
+
+// Two floats as one agent-scope atomic store (8-byte aligned address).
+__device__ __forceinline__ void store_pair_agent(float* p, float lo, float hi) {
+  const uint64_t v = uint64_t(__float_as_uint(lo)) | (uint64_t(__float_as_uint(hi)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int KVT, int G>
@@ -186,24 +196,23 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
       for (int e = 0; e < DPL; ++e) ored[wv][hh][d0 + e] = o[hh][e];
   __syncthreads();
 
-  // ---- this split's partials: o [j][s][G][D] and (m, l) [j][s][G][2]
+  // ---- this split's partials: o [j][s][G][D] and (m, l) [j][s][G][2], as
+  // agent-scope 64-bit atomic stores (pairs of floats)
   float* po = a.part + (size_t(j) * a.nsplit + s) * G * D;
   float* pml = a.part + size_t(a.nkv) * a.nsplit * G * D + (size_t(j) * a.nsplit + s) * G * 2;
-  for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+  auto osum = [&](int idx) {
     const int hh = idx / D, dd = idx % D;
-    po[idx] = ((ored[0][hh][dd] + ored[1][hh][dd]) + ored[2][hh][dd]) + ored[3][hh][dd];
-  }
-  if (threadIdx.x < G) {
-    pml[threadIdx.x * 2] = stat[threadIdx.x][0];
-    pml[threadIdx.x * 2 + 1] = stat[threadIdx.x][1];
-  }
+    return ((ored[0][hh][dd] + ored[1][hh][dd]) + ored[2][hh][dd]) + ored[3][hh][dd];
+  };
+  for (int i2 = threadIdx.x; i2 < G * D / 2; i2 += kBlock) store_pair_agent(po + 2 * i2, osum(2 * i2), osum(2 * i2 + 1));
+  if (threadIdx.x < G) store_pair_agent(pml + threadIdx.x * 2, stat[threadIdx.x][0], stat[threadIdx.x][1]);
 
   // ---- arrival: the last split of this kv head combines
-  __builtin_amdgcn_s_waitcnt(0);  // this lane's partial stores have completed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this lane's partial stores have completed
   __syncthreads();
+  uint32_t* cnt = a.counters + size_t(j) * kCounterStride;
   if (threadIdx.x == 0) {
-    const unsigned prev =
-        __hip_atomic_fetch_add(&a.counters[j], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last = (prev == unsigned(ns - 1));
   }
   __syncthreads();
@@ -269,7 +278,7 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
     const float r = 1.0f / den[hh];
     reinterpret_cast<float4*>(a.out + j * G * D)[f] = make_float4(acc.x * r, acc.y * r, acc.z * r, acc.w * r);
   }
-  if (threadIdx.x == 0) __hip_atomic_store(&a.counters[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 void attn_plan(int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit) {

@@ -8,6 +8,7 @@ namespace dec {
 
 constexpr uint32_t kErrPos = 0x1u;
 constexpr uint32_t kErrToken = 0x2u;
+constexpr int kCounterStride = 16;  // uint32 words between two kv heads' arrival counters (64 bytes)
 
 // Arguments of the GEMV-core kernels (passed by value).
 struct GemvArgs {
@@ -66,7 +67,7 @@ struct AttnArgs {
   const void* kc;      // [n_kv][max_ctx][d]
   const void* vc;
   float* part;         // [n_kv][S][g][d + 2]
-  uint32_t* counters;  // [n_kv]
+  uint32_t* counters;  // [n_kv * kCounterStride]
   float* out;          // [n_q d]
   const int32_t* pos;
   uint32_t* err;

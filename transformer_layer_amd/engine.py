@@ -61,7 +61,7 @@ class DecodeStack:
         self.attn = torch.zeros(c.q_dim, dtype=f32, device=dev)
         self.h = torch.zeros(c.ffn, dtype=f32, device=dev)
         self.part = torch.zeros(L.dec_attn_part_floats(self.desc), dtype=f32, device=dev)
-        self.counters = torch.zeros(c.n_kv_heads, dtype=torch.int32, device=dev)
+        self.counters = torch.zeros(c.n_kv_heads * L.DEC_COUNTER_STRIDE, dtype=torch.int32, device=dev)
         self.scratch = torch.zeros(L.dec_scratch_floats(self.desc), dtype=f32, device=dev)
         self.pos = torch.zeros(1, dtype=torch.int32, device=dev)
         self.token = torch.zeros(1, dtype=torch.int32, device=dev)

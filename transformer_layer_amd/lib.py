@@ -18,7 +18,8 @@ DEC_UNFUSED = 0x1
 DEC_NULL_KERNELS = 0x2
 DEC_ERR_POS = 0x1
 DEC_ERR_TOKEN = 0x2
-ABI_VERSION = 1
+ABI_VERSION = 2
+DEC_COUNTER_STRIDE = 16
 
 c_void_p, c_int32, c_uint32, c_float, c_double, c_int64 = (
     ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_double, ctypes.c_int64)
