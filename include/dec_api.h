@@ -68,13 +68,16 @@ enum dec_status {
   DEC_E_UNSUPPORTED = -6  /* valid request this build does not implement */
 };
 
-/* uint32 words per kv head in dec_layer_state.counters: each head's arrival
-   counter is word j * DEC_COUNTER_STRIDE, alone on its 64-byte line */
+/* uint32 words per kv head in dec_layer_state.counters: kv head j uses words
+   j * DEC_COUNTER_STRIDE (+0 arrivals, +1 finished combiners), alone on
+   their 64-byte line */
 #define DEC_COUNTER_STRIDE 16
 
 /* bits of the device error word */
 #define DEC_ERR_POS 0x1u
 #define DEC_ERR_TOKEN 0x2u
+#define DEC_ERR_SYNC 0x4u  /* an attention combiner stopped waiting for the other
+                              splits of its kv head; that output slice is not written */
 
 /* dec_layer_desc.flags */
 #define DEC_UNFUSED 0x1u       /* dec_layer_step runs the ten per-op kernels */

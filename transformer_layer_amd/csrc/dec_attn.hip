@@ -9,16 +9,19 @@
 // writes the split's partials: o (unnormalized) and (m, l). The first batch
 // of V rows is requested together with K.
 //
-// The last workgroup of a kv head to arrive combines the partials with a
-// log-sum-exp rescale. Ordering without an L2 write-back: the partials are
-// written with agent-scope atomic stores, which reach the device-coherent
-// level by themselves; every lane waits until its stores have completed
-// (vmcnt 0), the workgroup meets at a barrier, and one thread increments the
-// head's counter with an agent-scope atomic. Every counter sits on its own
-// 64-byte line, so the heads' arrivals do not queue on one line. The last
-// arriver's agent-scope acquire fence drops stale cached lines before it
-// reads the partials. The combiner resets the counter, so the kernel replays
-// unchanged inside a graph.
+// The last workgroups of a kv head to arrive (one per ~16 KB of partials, at
+// most kCombiners) combine its partials with a log-sum-exp rescale, each a
+// slice of the head group's outputs (one workgroup alone fetches the partials
+// too slowly). Ordering without an L2
+// write-back: the partials are written with agent-scope atomic stores, which
+// reach the device-coherent level by themselves; every lane waits until its
+// stores have completed (vmcnt 0), the workgroup meets at a barrier, and one
+// thread increments the head's arrival counter with an agent-scope atomic.
+// Combiners that arrive before the last one poll that counter (bounded: on
+// giving up they set DEC_ERR_SYNC and write nothing) and read the partials
+// with agent-scope loads. Every counter line is 64 bytes, so the heads'
+// arrivals do not queue on one line; the last combiner to finish resets the
+// line, so the kernel replays unchanged inside a graph.
 #include "dec_device.h"
 #include "dec_internal.h"
 
@@ -29,6 +32,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kChunkMax = 256;  // cache positions per split
 constexpr int kSplitMax = 256;  // splits per kv head
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kCombiners = 8;          // workgroups that combine one kv head's splits
+constexpr unsigned kSpinMax = 1u << 14;  // polls of a waiting combiner before it gives up
+constexpr int kNotCombiner = -1, kGaveUp = -2;   // workgroup roles after arrival (else the combiner slot)
 
 template <int KVT>
 __device__ __forceinline__ void unpack_row(u32x4 v, float* f) {
@@ -45,6 +51,13 @@ __device__ __forceinline__ void unpack_row(u32x4 v, float* f) {
 __device__ __forceinline__ void store_pair_agent(float* p, float lo, float hi) {
   const uint64_t v = uint64_t(__float_as_uint(lo)) | (uint64_t(__float_as_uint(hi)) << 32);
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Two floats with one agent-scope atomic load (8-byte aligned address).
+__device__ __forceinline__ float2 load_pair_agent(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
 }
 
 template <int D, int KVT, int G>
@@ -106,7 +119,7 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   __shared__ float sc[G][kChunkMax];
   __shared__ float stat[G][2];
   __shared__ float ored[kWaves][G][D];
-  __shared__ int last;
+  __shared__ int role;
 
   // ---- scores (log2 units): s_t = (q . k_t) log2(e) / sqrt(d)
   for (int b = 0; b < nsteps; b += U) {
@@ -207,89 +220,135 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   for (int i2 = threadIdx.x; i2 < G * D / 2; i2 += kBlock) store_pair_agent(po + 2 * i2, osum(2 * i2), osum(2 * i2 + 1));
   if (threadIdx.x < G) store_pair_agent(pml + threadIdx.x * 2, stat[threadIdx.x][0], stat[threadIdx.x][1]);
 
-  // ---- arrival: the last split of this kv head combines
+  // ---- arrival. The last ncomb splits of this kv head to arrive each
+  // combine a slice of its outputs: the earlier ones wait (bounded) until
+  // every split has arrived. Word 0 of the head's counter line counts
+  // arrivals, word 1 finished combiners; the last combiner to finish resets
+  // both for the next launch.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this lane's partial stores have completed
   __syncthreads();
   uint32_t* cnt = a.counters + size_t(j) * kCounterStride;
+  // one combiner per ~16 KB of partials (o of every split), at most kCombiners
+  int ncomb = ns * G * D / 4096;
+  ncomb = ncomb < 1 ? 1 : ncomb > kCombiners ? kCombiners : ncomb;
   if (threadIdx.x == 0) {
     const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last = (prev == unsigned(ns - 1));
-  }
-  __syncthreads();
-  if (!last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-  // per (split, head): weight w = exp2(m - M) and the denominator sum w l
-  __shared__ float wts[kSplitMax][G];
-  __shared__ float den[G];
-  const float* pj = a.part + size_t(j) * a.nsplit * G * D;
-  const float* mlj = a.part + size_t(a.nkv) * a.nsplit * G * D + size_t(j) * a.nsplit * G * 2;
-  for (int hh = wv; hh < G; hh += kWaves) {
-    float M = -INFINITY;
-    for (int t = lane; t < ns; t += kWave) M = fmaxf(M, mlj[(t * G + hh) * 2]);
-    M = wave_max(M);
-    float dsum = 0.0f;
-    for (int t = lane; t < ns; t += kWave) {
-      const float w = exp2f(mlj[(t * G + hh) * 2] - M);
-      wts[t][hh] = w;
-      dsum = fmaf(w, mlj[(t * G + hh) * 2 + 1], dsum);
-    }
-    dsum = wave_sum(dsum);
-    if (lane == 0) den[hh] = dsum;
-  }
-  __syncthreads();
-  // outputs as float4 groups; each thread sums a strided subset of the splits
-  constexpr int NV = G * D / 4;                 // float4 outputs
-  constexpr int PARTS = kBlock / NV > 0 ? kBlock / NV : 1;
-  __shared__ float4 accs[PARTS > 1 ? PARTS : 1][NV];
-  for (int f = threadIdx.x % NV; f < NV; f += kBlock) {
-    const int part = threadIdx.x / NV;
-    if (part >= PARTS) break;
-    const int hh = (f * 4) / D;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int t = part;
-    for (; t + 3 * PARTS < ns; t += 4 * PARTS) {
-      float4 v[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = reinterpret_cast<const float4*>(pj + size_t(t + k * PARTS) * G * D)[f];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float w = wts[t + k * PARTS][hh];
-        acc.x = fmaf(v[k].x, w, acc.x); acc.y = fmaf(v[k].y, w, acc.y);
-        acc.z = fmaf(v[k].z, w, acc.z); acc.w = fmaf(v[k].w, w, acc.w);
+    const int slot = int(prev) - (ns - ncomb);   // combiner slot; negative: not a combiner
+    bool gave_up = false;
+    if (slot >= 0 && prev != unsigned(ns - 1)) {
+      unsigned n = 0;
+      while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < unsigned(ns)) {
+        if (++n > kSpinMax) {   // give up: flag it, write nothing, still count as finished
+          atomicOr(a.err, kErrSync);
+          gave_up = true;
+          break;
+        }
       }
     }
-    for (; t < ns; t += PARTS) {
-      const float4 v = reinterpret_cast<const float4*>(pj + size_t(t) * G * D)[f];
-      const float w = wts[t][hh];
-      acc.x = fmaf(v.x, w, acc.x); acc.y = fmaf(v.y, w, acc.y);
-      acc.z = fmaf(v.z, w, acc.z); acc.w = fmaf(v.w, w, acc.w);
-    }
-    accs[part][f] = acc;
+    role = slot < 0 ? kNotCombiner : gave_up ? kGaveUp : slot;
   }
   __syncthreads();
-  for (int f = threadIdx.x; f < NV; f += kBlock) {
-    const int hh = (f * 4) / D;
-    float4 acc = accs[0][f];
-    for (int p = 1; p < PARTS; ++p) {
-      const float4 v = accs[p][f];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  const int w = role;
+  if (w == kNotCombiner) return;
+
+  if (w >= 0) {
+    // per (split, head): weight exp2(m - M) and the denominator sum of weight * l,
+    // read with agent-scope loads (the partials of other workgroups)
+    __shared__ float wts[kSplitMax][G];
+    __shared__ float den[G];
+    const float* pj = a.part + size_t(j) * a.nsplit * G * D;
+    const float* mlj = a.part + size_t(a.nkv) * a.nsplit * G * D + size_t(j) * a.nsplit * G * 2;
+    for (int hh = wv; hh < G; hh += kWaves) {
+      float2 ml[kSplitMax / kWave];
+      float M = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kSplitMax / kWave; ++k) {
+        const int t = lane + k * kWave;
+        ml[k] = t < ns ? load_pair_agent(mlj + (t * G + hh) * 2) : make_float2(-INFINITY, 0.0f);
+        M = fmaxf(M, ml[k].x);
+      }
+      M = wave_max(M);
+      float dsum = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kSplitMax / kWave; ++k) {
+        const int t = lane + k * kWave;
+        if (t < ns) {
+          const float wt = exp2f(ml[k].x - M);
+          wts[t][hh] = wt;
+          dsum = fmaf(wt, ml[k].y, dsum);
+        }
+      }
+      dsum = wave_sum(dsum);
+      if (lane == 0) den[hh] = dsum;
     }
-    const float r = 1.0f / den[hh];
-    reinterpret_cast<float4*>(a.out + j * G * D)[f] = make_float4(acc.x * r, acc.y * r, acc.z * r, acc.w * r);
+    __syncthreads();
+    // this combiner's slice of the float4 outputs; `parts` threads share an
+    // output, each summing every parts-th split, then meet in LDS
+    constexpr int NV = G * D / 4;
+    const int f0 = w * NV / ncomb, f1 = (w + 1) * NV / ncomb;
+    const int len = f1 - f0;
+    const int parts = kBlock / len;
+    __shared__ float4 accs[kBlock];
+    const int fi = threadIdx.x % len, part = threadIdx.x / len;
+    if (part < parts) {
+      const int f = f0 + fi;
+      const int hh = (f * 4) / D;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      int t = part;
+      for (; t + 3 * parts < ns; t += 4 * parts) {
+        float4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float* pv = pj + size_t(t + k * parts) * G * D + f * 4;
+          const float2 lo = load_pair_agent(pv), hi = load_pair_agent(pv + 2);
+          v[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float wt = wts[t + k * parts][hh];
+          acc.x = fmaf(v[k].x, wt, acc.x); acc.y = fmaf(v[k].y, wt, acc.y);
+          acc.z = fmaf(v[k].z, wt, acc.z); acc.w = fmaf(v[k].w, wt, acc.w);
+        }
+      }
+      for (; t < ns; t += parts) {
+        const float* pv = pj + size_t(t) * G * D + f * 4;
+        const float2 lo = load_pair_agent(pv), hi = load_pair_agent(pv + 2);
+        const float wt = wts[t][hh];
+        acc.x = fmaf(lo.x, wt, acc.x); acc.y = fmaf(lo.y, wt, acc.y);
+        acc.z = fmaf(hi.x, wt, acc.z); acc.w = fmaf(hi.y, wt, acc.w);
+      }
+      accs[part * len + fi] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x < len) {
+      const int f = f0 + threadIdx.x;
+      const int hh = (f * 4) / D;
+      float4 acc = accs[threadIdx.x];
+      for (int p = 1; p < parts; ++p) {
+        const float4 v = accs[p * len + threadIdx.x];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      const float r = 1.0f / den[hh];
+      reinterpret_cast<float4*>(a.out + j * G * D)[f] = make_float4(acc.x * r, acc.y * r, acc.z * r, acc.w * r);
+    }
   }
-  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    if (__hip_atomic_fetch_add(cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == unsigned(ncomb - 1)) {
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 void attn_plan(int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit) {
   int c = chunk_req;
   if (c <= 0) {
-    // about two workgroups per compute unit over the whole cache (at most
+    // about one workgroup per compute unit over the whole cache (at most
     // 64 splits per kv head), chunks a multiple of 16 rows and no longer
     // than one batch of rows in flight
     const int lanes_per_row = head_dim * (kvtype == 1 ? 2 : 4) / 16;
     const int one_batch = (kWave / lanes_per_row) * kWaves * 8;
-    int splits = 512 / n_kv;
+    int splits = 256 / n_kv;
     if (splits > 64) splits = 64;
     if (splits < 1) splits = 1;
     c = (max_ctx + splits - 1) / splits;

@@ -127,8 +127,21 @@ __device__ __forceinline__ void load_norm_granule(const void* g, int ntype, int 
 // head (QKV), a gate row and an up row (gated FFN), or two consecutive rows.
 // PF: the next task's weights are requested before the current task is
 // reduced (more bytes in flight per wave, more registers).
+// Resident waves per SIMD the compiler must keep for bf16 weights (a
+// register budget that holds without spills; the lane's input slice of
+// NJ * 8 floats dominates the register use). Other weight types are left to
+// the compiler.
+template <class T, int NJ, int KS, int EPI>
+constexpr int gemv_min_waves() {
+  if (T::ID != 1) return 1;
+  if (NJ <= 2) return (EPI == EPI_RESIDUAL || EPI == EPI_QKV) ? 4 : 5;
+  if (NJ <= 6) return (KS == 4 && EPI != EPI_QKV) ? 3 : 2;
+  return 2;
+}
+
 template <class T, int NJ, int KS, int EPI, int NP, bool PF>
-__global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(gemv_min_waves<T, NJ, KS, EPI>())))
+void gemv_kernel(GemvArgs a) {
   constexpr int GE = T::GE;
   constexpr int NR = 2 * NP;  // rows per task
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_NORM_STORE);
@@ -208,8 +221,12 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
   float sc[NR][NJ];
   load_task(blockIdx.x * TPW + slot, wq, sc);
 
-  // ---- prologue: this lane's slice of the input vector, in registers
+  // ---- prologue: this lane's slice of the input vector, in registers. The
+  // norm weights are requested together with it when they fit in registers
+  // (they do not depend on the sum of squares).
+  constexpr bool EARLY_NORM = NORM && !Q4 && NJ * GE <= 32;
   float u[NJ][GE];
+  float gw[EARLY_NORM ? NJ : 1][EARLY_NORM ? GE : 1];
   float usum[NJ];
   float ss = 0.0f;
 #pragma unroll
@@ -223,12 +240,16 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
       u[j][e] = ok ? v.x : 0.0f; u[j][e + 1] = ok ? v.y : 0.0f;
       u[j][e + 2] = ok ? v.z : 0.0f; u[j][e + 3] = ok ? v.w : 0.0f;
     }
-    if constexpr (NORM) {
+    if constexpr (EARLY_NORM) load_norm_granule<GE>(a.norm, a.ntype, gc, gw[j]);
+  }
+  if constexpr (NORM) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < GE; ++e) ss = fmaf(u[j][e], u[j][e], ss);
-    }
   }
   constexpr int kBatch = 16;  // tasks per LDS batch (column-split waves)
+  static_assert(kBatch * NP <= kWave, "one batch item per lane of the finishing wave");
   __shared__ float red[KS > 1 ? kWaves : 1][KS > 1 ? kBatch : 1][NR];
   __shared__ float ssq[kWaves];
   if constexpr (NORM) {
@@ -245,7 +266,12 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
     for (int j = 0; j < NJ; ++j) {
       const int gi = (j * KS + ks) * kWave + lane;
       float g[GE];
-      load_norm_granule<GE>(a.norm, a.ntype, gi < G ? gi : G - 1, g);
+      if constexpr (EARLY_NORM) {
+#pragma unroll
+        for (int e = 0; e < GE; ++e) g[e] = gw[j][e];
+      } else {
+        load_norm_granule<GE>(a.norm, a.ntype, gi < G ? gi : G - 1, g);
+      }
 #pragma unroll
       for (int e = 0; e < GE; ++e) u[j][e] = (u[j][e] * r) * g[e];   // u is 0 past the row end
     }
@@ -260,8 +286,26 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
     }
   }
 
+  // ---- inputs of a pair's epilogue that do not depend on the dot products
+  // (the residual's old x values; RoPE's cos and sin), requested when the
+  // task starts by the lane that will finish the pair, so no load is left
+  // for the end of the task
+  auto epi_inputs = [&](int p, float& e0, float& e1) {
+    if (p >= npairs) return;
+    int r0, r1;
+    rows_of(p, r0, r1);
+    if constexpr (EPI == EPI_RESIDUAL) {
+      e0 = r0 < a.rows ? a.x[r0] : 0.0f;
+      e1 = r1 < a.rows ? a.x[r1] : 0.0f;
+    } else if constexpr (EPI == EPI_QKV) {
+      const int i = p % half;
+      e0 = a.rope[(size_t(pos) * half + i) * 2];
+      e1 = a.rope[(size_t(pos) * half + i) * 2 + 1];
+    }
+  };
+
   // ---- epilogue of one row pair (run by one lane)
-  auto epilogue = [&](int p, float y0, float y1) {
+  auto epilogue = [&](int p, float y0, float y1, float e0, float e1) {
     if (p >= npairs) return;
     int r0, r1;
     rows_of(p, r0, r1);
@@ -271,8 +315,8 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
       if (v0) a.y[r0] = y0;
       if (v1) a.y[r1] = y1;
     } else if constexpr (EPI == EPI_RESIDUAL) {
-      if (v0) a.x[r0] += y0;
-      if (v1) a.x[r1] += y1;
+      if (v0) a.x[r0] = e0 + y0;
+      if (v1) a.x[r1] = e1 + y1;
     } else if constexpr (EPI == EPI_SWIGLU) {
       a.y[r0] = swiglu(y0, y1);
     } else if constexpr (EPI == EPI_STORE2) {
@@ -281,11 +325,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
     } else {  // EPI_QKV
       const int head = p / half;
       const int i = p % half;
-      if (head < a.nq + a.nkv) {
-        const float c = a.rope[(size_t(pos) * half + i) * 2];
-        const float s = a.rope[(size_t(pos) * half + i) * 2 + 1];
-        rope_rotate(y0, y1, c, s);
-      }
+      if (head < a.nq + a.nkv) rope_rotate(y0, y1, e0, e1);
       if (head < a.nq) {
         a.y[r0] = y0;
         a.y[r1] = y1;
@@ -310,9 +350,20 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
   // ---- tasks: this wave slot handles task, task + stride, ...
   int nb = 0;                         // tasks in the current LDS batch
   int batch_base = blockIdx.x * TPW;  // base of its first task
+  constexpr bool EPI_IN = (EPI == EPI_RESIDUAL || EPI == EPI_QKV);
+  float ex0 = 0.0f, ex1 = 0.0f;       // epilogue inputs of the pair this lane finishes
   for (int base = blockIdx.x * TPW; base < a.ntask; base += stride) {
     const int task = base + slot;
     const bool more = base + stride < a.ntask;
+    if constexpr (EPI_IN) {
+      if constexpr (KS == 1) {
+        if (lane < NP && task < a.ntask) epi_inputs(task * NP + lane, ex0, ex1);
+      } else {
+        // lane nb*NP + q of wave ks == 0 finishes pair q of this task (batch item nb)
+        const int q = lane - nb * NP;
+        if (ks == 0 && q >= 0 && q < NP && task < a.ntask) epi_inputs(task * NP + q, ex0, ex1);
+      }
+    }
     u32x4 wn[PF ? NR : 1][NJ];
     float sn[PF ? NR : 1][NJ];
     if constexpr (PF) {
@@ -361,7 +412,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
 #pragma unroll
         for (int q = 1; q < NP; ++q)
           if (lane == q) { y0 = acc[2 * q]; y1 = acc[2 * q + 1]; }
-        epilogue(task * NP + lane, y0, y1);
+        if (task < a.ntask) epilogue(task * NP + lane, y0, y1, ex0, ex1);
       }
     } else {
       // partial sums of the KS waves meet in LDS; finished in batches so the
@@ -373,18 +424,16 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(GemvArgs a) {
       ++nb;
       if (nb == kBatch || !more) {
         __syncthreads();
-        if (ks == 0) {
-          for (int e = lane; e < nb * NP; e += kWave) {
-            const int bi = e / NP, q = e % NP;
-            const int t = batch_base + bi * stride + slot;
-            float s0 = 0.0f, s1 = 0.0f;
+        if (ks == 0 && lane < nb * NP) {   // nb * NP <= kBatch * 2 < kWave: one item per lane
+          const int bi = lane / NP, q = lane % NP;
+          const int t = batch_base + bi * stride + slot;
+          float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-            for (int k = 0; k < KS; ++k) {
-              s0 += red[slot * KS + k][bi][2 * q];
-              s1 += red[slot * KS + k][bi][2 * q + 1];
-            }
-            if (t < a.ntask) epilogue(t * NP + q, s0, s1);
+          for (int k = 0; k < KS; ++k) {
+            s0 += red[slot * KS + k][bi][2 * q];
+            s1 += red[slot * KS + k][bi][2 * q + 1];
           }
+          if (t < a.ntask) epilogue(t * NP + q, s0, s1, ex0, ex1);
         }
         __syncthreads();
         nb = 0;

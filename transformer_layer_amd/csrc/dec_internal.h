@@ -8,6 +8,7 @@ namespace dec {
 
 constexpr uint32_t kErrPos = 0x1u;
 constexpr uint32_t kErrToken = 0x2u;
+constexpr uint32_t kErrSync = 0x4u;
 constexpr int kCounterStride = 16;  // uint32 words between two kv heads' arrival counters (64 bytes)
 
 // Arguments of the GEMV-core kernels (passed by value).

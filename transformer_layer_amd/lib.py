@@ -18,6 +18,7 @@ DEC_UNFUSED = 0x1
 DEC_NULL_KERNELS = 0x2
 DEC_ERR_POS = 0x1
 DEC_ERR_TOKEN = 0x2
+DEC_ERR_SYNC = 0x4
 ABI_VERSION = 2
 DEC_COUNTER_STRIDE = 16
 
