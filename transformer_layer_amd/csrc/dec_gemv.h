@@ -443,22 +443,33 @@ void gemv_kernel(GemvArgs a) {
   }
 }
 
+// Workgroups that one kernel keeps resident on the current device
+// (occupancy x compute units), cached per (device, kernel): every GEMV
+// instantiation has its own register use and so its own occupancy.
+template <class K>
+inline int resident_blocks(K kernel) {
+  struct Entry { const void* fn; int dev; int cap; };
+  static thread_local Entry cache[128];
+  static thread_local int used = 0;
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].fn == fn && cache[i].dev == dev) return cache[i].cap;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  const int cap = per_cu * cus;
+  if (used < 128) cache[used++] = Entry{fn, dev, cap};
+  return cap;
+}
+
 // Workgroups for `groups` task groups: at most what the device keeps resident
 // (occupancy x compute units), with the groups spread evenly over them.
 template <class K>
 inline int gemv_grid(K kernel, int groups) {
-  static thread_local int resident[64] = {0};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  int& cap = resident[dev & 63];
-  if (cap == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || per_cu < 1)
-      per_cu = 1;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      cus = 256;
-    cap = per_cu * cus;
-  }
+  const int cap = resident_blocks(kernel);
   const int per_wg = (groups + cap - 1) / cap;
   return (groups + per_wg - 1) / per_wg;
 }
