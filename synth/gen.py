@@ -9,12 +9,11 @@ Distributions (the decode workloads' stated recipe):
 
 * projection and LM-head weights: N(0, 0.02^2), drawn as fp32 and stored as
   fp32, bf16 (round to nearest even) or 4-bit blocks;
-* 4-bit blocks (the workloads): N(0, 0.02^2) weights quantized per block of
-  32 along the input dimension as a symmetric 4-bit quantizer does: fp16
-  scale = max|w| / 7, code = round(w / scale) clipped to [-8, 7] (so the
-  codes are zero-mean, like quantized trained weights). Test matrices may
-  instead draw codes uniformly over the whole range [-8, 7] with scales
-  |N(0, 0.02^2)| / 7, to cover every code. Nibble layout: element 2i is the
+* 4-bit blocks: 32 signed int4 codes per block along the input dimension,
+  one fp16 scale per block drawn as |N(0, 0.02^2)| / 7. Workload codes are
+  uniform over the symmetric range [-7, 7] (zero-mean, like the codes of
+  quantized trained weights); test matrices may draw them uniformly over the
+  whole range [-8, 7] to cover every code. Nibble layout: element 2i is the
   low nibble of byte i, element 2i+1 the high nibble;
 * norm weights: 1 + N(0, 0.01^2);
 * token embedding table: N(0, 1), fp32;
@@ -118,11 +117,11 @@ def _normal_rows(key, rows: int, cols: int, std: float, mean: float, kind: str) 
     return Stored(kind, out)
 
 
-def _q4_rows(key, rows: int, cols: int, std: float, codes: str = "quantized") -> Stored:
+def _q4_rows(key, rows: int, cols: int, std: float, codes: str = "symmetric") -> Stored:
     """rows x cols of 4-bit block-quantized weights (see module docstring).
-    codes="quantized": N(0, std^2) weights through a symmetric per-block
-    quantizer; codes="uniform": codes uniform over [-8, 7]."""
-    assert cols % 32 == 0 and codes in ("quantized", "uniform")
+    codes="symmetric": uniform over [-7, 7]; codes="uniform": uniform over [-8, 7]."""
+    assert cols % 32 == 0 and codes in ("symmetric", "uniform")
+    lo = -8 if codes == "uniform" else -7
     rpc = max(1, CHUNK_ELEMS // cols)
     nchunk = (rows + rpc - 1) // rpc
     nib = np.empty((rows, cols // 2), dtype=np.uint8)
@@ -131,20 +130,11 @@ def _q4_rows(key, rows: int, cols: int, std: float, codes: str = "quantized") ->
     def work(ci: int) -> None:
         r0 = ci * rpc
         r1 = min(rows, r0 + rpc)
-        n = r1 - r0
-        if codes == "uniform":
-            c = _rng(key, ci, 0).integers(-8, 8, size=(n, cols), dtype=np.int8)
-            z = _rng(key, ci, 1).standard_normal((n, cols // 32), dtype=np.float32)
-            sc[r0:r1] = (np.abs(z) * np.float32(std) / np.float32(7.0)).astype(np.float16)
-        else:
-            w = _rng(key, ci, 0).standard_normal((n, cols // 32, 32), dtype=np.float32) * np.float32(std)
-            s16 = (np.abs(w).max(axis=2) / np.float32(7.0)).astype(np.float16)
-            s32 = s16.astype(np.float32)
-            s32[s32 == 0] = 1.0
-            c = np.clip(np.rint(w / s32[:, :, None]), -8, 7).astype(np.int8).reshape(n, cols)
-            sc[r0:r1] = s16
+        c = _rng(key, ci, 0).integers(lo, 8, size=(r1 - r0, cols), dtype=np.int8)
         u = c.view(np.uint8) & np.uint8(0x0F)
         nib[r0:r1] = u[:, 0::2] | (u[:, 1::2] << np.uint8(4))
+        z = _rng(key, ci, 1).standard_normal((r1 - r0, cols // 32), dtype=np.float32)
+        sc[r0:r1] = (np.abs(z) * np.float32(std) / np.float32(7.0)).astype(np.float16)
 
     list(_pool().map(work, range(nchunk)))
     return Stored("q4", nib, sc)
@@ -231,7 +221,7 @@ def rand_f32(key, shape, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
 def rand_matrix(key, rows: int, cols: int, kind: str, std: float = 0.02, q4_codes: str = "uniform") -> Stored:
     """A seeded weight matrix in storage encoding `kind` (test inputs); 4-bit
     test matrices draw their codes uniformly over [-8, 7] unless q4_codes is
-    "quantized"."""
+    "symmetric" (the workloads' [-7, 7])."""
     if kind == "q4":
         return _q4_rows(tuple(key), rows, cols, std, q4_codes)
     return _normal_rows(tuple(key), rows, cols, std, 0.0, kind)
