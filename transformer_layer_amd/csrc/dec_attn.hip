@@ -7,9 +7,9 @@
 // kept in LDS, in log2 units), turns them into exp2(s - m) with one
 // exponential per (head, position), reads the same chunk of V once, and
 // writes the split's partials: o (unnormalized) and (m, l). The first batch
-// of V rows is requested together with K.
+// of V rows is requested right after the K rows.
 //
-// The last workgroups of a kv head to arrive (one per ~16 KB of partials, at
+// The last workgroups of a kv head to arrive (one per ~8 KB of partials, at
 // most kCombiners) combine its partials with a log-sum-exp rescale, each a
 // slice of the head group's outputs (one workgroup alone fetches the partials
 // too slowly). Ordering without an L2
@@ -96,13 +96,19 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   const u32x4 z = {0u, 0u, 0u, 0u};
   auto row = [&](int step) { return t0 + step * RPS + wv * RPW + sub; };
 
-  // first batch of K and V rows, then the queries
+  // first batch of K rows, then of V rows (the scores need only K, so they
+  // start while V is still arriving), then the queries
   u32x4 kv[U], vv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int t = row(u);
     const bool ok = u < nsteps && t < t1;
     kv[u] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + d0) * EB) : z;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int t = row(u);
+    const bool ok = u < nsteps && t < t1;
     vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
   }
   const float qscale = kLog2e / sqrtf(float(D));
@@ -197,11 +203,9 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   }
   // rows of one wave load sit LPR lanes apart: fold them
 #pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1)
+  for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o[hh][e] += __shfl_xor(o[hh][e], off);
+    for (int e = 0; e < DPL; ++e) o[hh][e] = fold_groups<LPR>(o[hh][e]);
   if (sub == 0)
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
@@ -228,8 +232,8 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this lane's partial stores have completed
   __syncthreads();
   uint32_t* cnt = a.counters + size_t(j) * kCounterStride;
-  // one combiner per ~16 KB of partials (o of every split), at most kCombiners
-  int ncomb = ns * G * D / 4096;
+  // one combiner per ~8 KB of partials (o of every split), at most kCombiners
+  int ncomb = ns * G * D / 2048;
   ncomb = ncomb < 1 ? 1 : ncomb > kCombiners ? kCombiners : ncomb;
   if (threadIdx.x == 0) {
     const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

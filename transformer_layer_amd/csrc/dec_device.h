@@ -24,10 +24,46 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // DPP lane moves inside one 16-lane row. Controls: quad_perm [1,0,3,2] = 0xB1,
-// quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
+// quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140,
+// row_ror:8 = 0x128.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Values of lanes l and l ^ 16 (k = 16) or l and l ^ 32 (k = 32), as a pair
+// that every lane of the two receives in the same order (lower lane first):
+// v_permlane16_swap exchanges the odd 16-lane rows of one operand with the
+// even rows of the other, v_permlane32_swap the upper half of one with the
+// lower half of the other; with both operands v, the two results are the
+// pair. No LDS traffic, unlike a shuffle through ds_bpermute.
+template <int K>
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+  static_assert(K == 16 || K == 32, "pair distance");
+  const uint32_t b = __float_as_uint(v);
+  if constexpr (K == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  }
+}
+
+template <int K>
+__device__ __forceinline__ float pair_sum(float v) {
+  float lo, hi;
+  lane_pair<K>(v, lo, hi);
+  return lo + hi;
+}
+
+template <int K>
+__device__ __forceinline__ float pair_max(float v) {
+  float lo, hi;
+  lane_pair<K>(v, lo, hi);
+  return fmaxf(lo, hi);
 }
 
 // Sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32, 64); every lane of
@@ -39,8 +75,8 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (N >= 4) v += dpp_mov<0x4E>(v);
   if constexpr (N >= 8) v += dpp_mov<0x141>(v);
   if constexpr (N >= 16) v += dpp_mov<0x140>(v);
-  if constexpr (N >= 32) v += __shfl_xor(v, 16);
-  if constexpr (N >= 64) v += __shfl_xor(v, 32);
+  if constexpr (N >= 32) v = pair_sum<16>(v);
+  if constexpr (N >= 64) v = pair_sum<32>(v);
   return v;
 }
 
@@ -50,9 +86,20 @@ __device__ __forceinline__ float group_max(float v) {
   if constexpr (N >= 4) v = fmaxf(v, dpp_mov<0x4E>(v));
   if constexpr (N >= 8) v = fmaxf(v, dpp_mov<0x141>(v));
   if constexpr (N >= 16) v = fmaxf(v, dpp_mov<0x140>(v));
-  if constexpr (N >= 32) v = fmaxf(v, __shfl_xor(v, 16));
-  if constexpr (N >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+  if constexpr (N >= 32) v = pair_max<16>(v);
+  if constexpr (N >= 64) v = pair_max<32>(v);
   return v;
+}
+
+// Sum of v over the lanes l, l ^ S, l ^ 2S, ... (S = 8, 16 or 32): folds the
+// groups of S lanes of a wave onto each other lane by lane. row_ror:8
+// (0x128) gives lane l ^ 8 inside a 16-lane row.
+template <int S>
+__device__ __forceinline__ float fold_groups(float v) {
+  static_assert(S == 8 || S == 16 || S == 32, "group width");
+  if constexpr (S <= 8) v += dpp_mov<0x128>(v);
+  if constexpr (S <= 16) v = pair_sum<16>(v);
+  return pair_sum<32>(v);
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
