@@ -256,12 +256,35 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   if (w == kNotCombiner) return;
 
   if (w >= 0) {
+    const float* pj = a.part + size_t(j) * a.nsplit * G * D;
+    const float* mlj = a.part + size_t(a.nkv) * a.nsplit * G * D + size_t(j) * a.nsplit * G * 2;
+    // this combiner's slice of the float4 outputs; `parts` threads share an
+    // output, each summing every parts-th split, then meet in LDS. The first
+    // kPre splits of each thread are requested before the (m, l) pass, so
+    // both round trips overlap.
+    constexpr int NV = G * D / 4;
+    constexpr int kPre = 8;
+    const int f0 = w * NV / ncomb, f1 = (w + 1) * NV / ncomb;
+    const int len = f1 - f0;
+    const int parts = kBlock / len;
+    const int fi = threadIdx.x % len, part = threadIdx.x / len;
+    const bool active = part < parts;
+    const int f = f0 + fi;
+    float4 pre[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int t = part + k * parts;
+      pre[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (active && t < ns) {
+        const float* pv = pj + size_t(t) * G * D + f * 4;
+        const float2 lo = load_pair_agent(pv), hi = load_pair_agent(pv + 2);
+        pre[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
     // per (split, head): weight exp2(m - M) and the denominator sum of weight * l,
     // read with agent-scope loads (the partials of other workgroups)
     __shared__ float wts[kSplitMax][G];
     __shared__ float den[G];
-    const float* pj = a.part + size_t(j) * a.nsplit * G * D;
-    const float* mlj = a.part + size_t(a.nkv) * a.nsplit * G * D + size_t(j) * a.nsplit * G * 2;
     for (int hh = wv; hh < G; hh += kWaves) {
       float2 ml[kSplitMax / kWave];
       float M = -INFINITY;
@@ -286,35 +309,18 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
       if (lane == 0) den[hh] = dsum;
     }
     __syncthreads();
-    // this combiner's slice of the float4 outputs; `parts` threads share an
-    // output, each summing every parts-th split, then meet in LDS
-    constexpr int NV = G * D / 4;
-    const int f0 = w * NV / ncomb, f1 = (w + 1) * NV / ncomb;
-    const int len = f1 - f0;
-    const int parts = kBlock / len;
     __shared__ float4 accs[kBlock];
-    const int fi = threadIdx.x % len, part = threadIdx.x / len;
-    if (part < parts) {
-      const int f = f0 + fi;
+    if (active) {
       const int hh = (f * 4) / D;
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      int t = part;
-      for (; t + 3 * parts < ns; t += 4 * parts) {
-        float4 v[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float* pv = pj + size_t(t + k * parts) * G * D + f * 4;
-          const float2 lo = load_pair_agent(pv), hi = load_pair_agent(pv + 2);
-          v[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float wt = wts[t + k * parts][hh];
-          acc.x = fmaf(v[k].x, wt, acc.x); acc.y = fmaf(v[k].y, wt, acc.y);
-          acc.z = fmaf(v[k].z, wt, acc.z); acc.w = fmaf(v[k].w, wt, acc.w);
-        }
+      for (int k = 0; k < kPre; ++k) {
+        const int t = part + k * parts;
+        const float wt = t < ns ? wts[t][hh] : 0.0f;
+        acc.x = fmaf(pre[k].x, wt, acc.x); acc.y = fmaf(pre[k].y, wt, acc.y);
+        acc.z = fmaf(pre[k].z, wt, acc.z); acc.w = fmaf(pre[k].w, wt, acc.w);
       }
-      for (; t < ns; t += parts) {
+      for (int t = part + kPre * parts; t < ns; t += parts) {
         const float* pv = pj + size_t(t) * G * D + f * 4;
         const float2 lo = load_pair_agent(pv), hi = load_pair_agent(pv + 2);
         const float wt = wts[t][hh];

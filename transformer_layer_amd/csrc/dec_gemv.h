@@ -151,7 +151,7 @@ void gemv_kernel(GemvArgs a) {
 
   if (a.null_kernel) return;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform: row addresses stay scalar
   const int ks = wv % KS;
   const int slot = wv / KS;
 
