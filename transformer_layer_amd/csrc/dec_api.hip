@@ -47,8 +47,9 @@ int check_desc(const dec_layer_desc* d) {
   if (d->max_ctx <= 0 || d->max_ctx > (1 << 20)) return fail(DEC_E_SHAPE, "max_ctx %d", d->max_ctx);
   if (!(d->rms_eps >= 0.0f)) return fail(DEC_E_SHAPE, "rms_eps");
   if (d->attn_chunk < 0 || d->attn_chunk > 256) return fail(DEC_E_SHAPE, "attn_chunk %d (0..256)", d->attn_chunk);
-  int chunk, ns;
-  dec::attn_plan(d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk, &chunk, &ns);
+  int chunk, ns, nw;
+  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
+                 &chunk, &ns, &nw);
   if (ns > 256) return fail(DEC_E_SHAPE, "max_ctx %d needs %d splits (max 256)", d->max_ctx, ns);
   return DEC_OK;
 }
@@ -118,7 +119,8 @@ int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t 
   a.max_ctx = d->max_ctx;
   a.kvtype = d->kvtype == DEC_BF16 ? 1 : 0;
   a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
-  dec::attn_plan(d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk, &a.chunk, &a.nsplit);
+  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
+                 &a.chunk, &a.nsplit, &a.waves);
   return launched(dec::launch_attn(a, s), "attn_splitk");
 }
 
@@ -188,8 +190,9 @@ const char* dec_last_error(void) { return g_err; }
 
 int64_t dec_attn_part_floats(const dec_layer_desc* d) {
   if (check_desc(d)) return -1;
-  int chunk, ns;
-  dec::attn_plan(d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk, &chunk, &ns);
+  int chunk, ns, nw;
+  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
+                 &chunk, &ns, &nw);
   return int64_t(d->n_q_heads) * ns * (d->head_dim + 2);
 }
 

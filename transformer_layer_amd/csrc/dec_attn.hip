@@ -60,8 +60,10 @@ __device__ __forceinline__ float2 load_pair_agent(const float* p) {
   return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
 }
 
-template <int D, int KVT, int G>
-__global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
+template <int D, int KVT, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
+  constexpr int kWaves = NW;        // waves per workgroup (4 or 8)
+  constexpr int kBlock = NW * 64;
   constexpr int EB = KVT == 1 ? 2 : 4;  // bytes per cache element
   constexpr int DPL = 16 / EB;          // dims per lane
   constexpr int LPR = D / DPL;          // lanes per cache row
@@ -219,7 +221,10 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   float* pml = a.part + size_t(a.nkv) * a.nsplit * G * D + (size_t(j) * a.nsplit + s) * G * 2;
   auto osum = [&](int idx) {
     const int hh = idx / D, dd = idx % D;
-    return ((ored[0][hh][dd] + ored[1][hh][dd]) + ored[2][hh][dd]) + ored[3][hh][dd];
+    float r = ored[0][hh][dd];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r += ored[w][hh][dd];
+    return r;
   };
   for (int i2 = threadIdx.x; i2 < G * D / 2; i2 += kBlock) store_pair_agent(po + 2 * i2, osum(2 * i2), osum(2 * i2 + 1));
   if (threadIdx.x < G) store_pair_agent(pml + threadIdx.x * 2, stat[threadIdx.x][0], stat[threadIdx.x][1]);
@@ -350,20 +355,29 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnArgs a) {
   }
 }
 
-void attn_plan(int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit) {
+void attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit,
+               int* waves) {
   int c = chunk_req;
+  int nw = 4;
   if (c <= 0) {
     // about one workgroup per compute unit over the whole cache (at most
     // 64 splits per kv head), chunks a multiple of 16 rows and no longer
     // than one batch of rows in flight
     const int lanes_per_row = head_dim * (kvtype == 1 ? 2 : 4) / 16;
-    const int one_batch = (kWave / lanes_per_row) * kWaves * 8;
+    const int one_batch = (kWave / lanes_per_row) * 4 * 8;
     int splits = 256 / n_kv;
     if (splits > 64) splits = 64;
     if (splits < 1) splits = 1;
     c = (max_ctx + splits - 1) / splits;
     c = ((c + 15) / 16) * 16;
     if (c > one_batch) c = one_batch;
+    // bf16 head_dim 128 with four or more query heads per kv head and up to
+    // 4608 positions (measured on the 9B-shaped layer): 192-row chunks over
+    // 8 waves, one batch per wave and fewer splits to combine
+    if (head_dim == 128 && kvtype == 1 && n_q >= 4 * n_kv && max_ctx <= 4608) {
+      nw = 8;
+      c = 192;
+    }
   }
   const int cmin = (max_ctx + kSplitMax - 1) / kSplitMax;
   if (c < cmin) c = cmin;
@@ -371,26 +385,34 @@ void attn_plan(int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, i
   if (c > kChunkMax) c = kChunkMax;
   *chunk = c;
   *nsplit = (max_ctx + c - 1) / c;
+  *waves = nw;
 }
 
-template <int D, int KVT>
+template <int D, int KVT, int NW>
 static hipError_t go_attn(const AttnArgs& a, hipStream_t s) {
   const int g = a.nq / a.nkv;
-  const dim3 grid(a.nkv * a.nsplit), block(kBlock);
+  const dim3 grid(a.nkv * a.nsplit), block(NW * 64);
   switch (g) {
-    case 1: hipLaunchKernelGGL((attn_kernel<D, KVT, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_kernel<D, KVT, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_kernel<D, KVT, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_kernel<D, KVT, 8>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((attn_kernel<D, KVT, 1, NW>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_kernel<D, KVT, 2, NW>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_kernel<D, KVT, 4, NW>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((attn_kernel<D, KVT, 8, NW>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int D, int KVT>
+static hipError_t go_attn_waves(const AttnArgs& a, hipStream_t s) {
+  if (a.waves == 8) return go_attn<D, KVT, 8>(a, s);
+  if (a.waves == 4) return go_attn<D, KVT, 4>(a, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (a.nsplit > kSplitMax || a.chunk > kChunkMax) return hipErrorInvalidValue;
-  if (a.d == 64) return a.kvtype == 1 ? go_attn<64, 1>(a, s) : go_attn<64, 0>(a, s);
-  if (a.d == 128) return a.kvtype == 1 ? go_attn<128, 1>(a, s) : go_attn<128, 0>(a, s);
+  if (a.d == 64) return a.kvtype == 1 ? go_attn_waves<64, 1>(a, s) : go_attn_waves<64, 0>(a, s);
+  if (a.d == 128) return a.kvtype == 1 ? go_attn_waves<128, 1>(a, s) : go_attn_waves<128, 0>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -73,11 +73,13 @@ struct AttnArgs {
   const int32_t* pos;
   uint32_t* err;
   int nq, nkv, d, max_ctx, chunk, nsplit, kvtype;
+  int waves;           // waves per workgroup (4 or 8)
   int null_kernel;
 };
 
-// attention chunk (positions per split) and split count for a shape
-void attn_plan(int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit);
+// attention chunk (positions per split), split count and waves per workgroup for a shape
+void attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit,
+               int* waves);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
 // small per-op and per-token kernels
