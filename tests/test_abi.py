@@ -257,3 +257,23 @@ def test_error_text_is_per_thread(L):
     t.join()
     assert "head_dim" in L.dec_last_error()
     assert seen == [""]
+
+
+def test_library_allocates_copies_and_synchronises_nothing(L):
+    """Every buffer comes from the caller: the HIP runtime functions the
+    library imports are kernel registration and launch, device and occupancy
+    queries and error reporting only. No allocation, free, memset, copy or
+    synchronisation can happen inside an entry point, so a decode step is
+    capturable into a graph as it stands."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", L.LIBPATH], capture_output=True, text=True)
+    if out.returncode != 0:
+        pytest.skip("nm unavailable")
+    imported = {ln.split()[-1].split("@")[0] for ln in out.stdout.splitlines() if ln.strip()}
+    hip = {s for s in imported if s.lower().startswith(("hip", "__hip"))}
+    allowed = {"__hipRegisterFatBinary", "__hipUnregisterFatBinary", "__hipRegisterFunction",
+               "__hipRegisterVar", "__hipPushCallConfiguration", "__hipPopCallConfiguration",
+               "hipLaunchKernel", "hipGetDevice", "hipDeviceGetAttribute", "hipGetLastError",
+               "hipGetErrorString", "hipOccupancyMaxActiveBlocksPerMultiprocessor"}
+    assert hip <= allowed, f"unexpected HIP runtime imports: {sorted(hip - allowed)}"
+    assert not {s for s in imported if s in ("malloc", "calloc", "realloc") or "Malloc" in s}, \
+        "the library should not allocate host memory either"

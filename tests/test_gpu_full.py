@@ -6,6 +6,9 @@ benchmark times (the same kernels, grids and split counts).
   run independently, and the cache slots the GPU wrote.
 * One decode token through the whole 40-layer 9B-shaped bf16 stack, layer by
   layer.
+* The five fused kernels against the ten per-op kernels at the 9B shapes
+  (bf16 and 4-bit weights, real cache lengths): hidden states and caches
+  equal bit for bit.
 * 64 greedy decode steps through the captured per-token graph (embedding,
   layers, LM head, argmax, next token on the device) against the oracle's
   greedy tokens stored under tests/golden/ (written by make_greedy.py, which
@@ -30,6 +33,7 @@ import torch
 import oracle
 import synth
 from helpers import check_rounded_slot, rel_l2
+from transformer_layer_amd import lib as L
 from transformer_layer_amd.engine import DecodeStack
 
 pytestmark = pytest.mark.gpu
@@ -113,6 +117,37 @@ def test_whole_9b_stack_one_token(gpu):
     assert st.check_err() == 0
     assert max(errs) <= TOL, f"worst layer {int(np.argmax(errs))}: {max(errs):.3e}"
     _release()
+
+
+@pytest.mark.parametrize("name", ["C4", "C5"])
+def test_fused_equals_unfused_bitwise_at_full_shape(gpu, name):
+    cfg = synth.CONFIGS[name]
+    nl, nsteps = 2, 3
+    toks = synth.tokens(cfg)
+    weights = [synth.layer_weights(cfg, l) for l in range(nl)]
+    pre = [synth.prefill(cfg, l) for l in range(nl)]
+    embed = synth.embedding(cfg)
+    outs = []
+    for flags in (0, L.DEC_UNFUSED):
+        st = DecodeStack(cfg, n_layers=nl, flags=flags)
+        for l in range(nl):
+            st.set_layer(l, weights[l])
+            st.set_prefill(l, *pre[l])
+        st.set_embedding(embed)
+        rec = torch.zeros(nl + 1, cfg.hidden, dtype=torch.float32, device="cuda")
+        xs = []
+        for i in range(nsteps):
+            st.set_pos(cfg.ctx + i)
+            st.set_token(int(toks[i]))
+            st.token_step(record=rec)
+            xs.append(rec.cpu().numpy().copy())
+        assert st.check_err() == 0
+        outs.append((np.stack(xs), st.K.cpu(), st.V.cpu()))
+        del st
+        _release()
+    (xa, Ka, Va), (xb, Kb, Vb) = outs
+    assert np.array_equal(xa.view(np.uint32), xb.view(np.uint32)), f"{name}: hidden states differ"
+    assert torch.equal(Ka, Kb) and torch.equal(Va, Vb), f"{name}: caches differ"
 
 
 GREEDY = sorted(os.path.basename(p)[len("greedy_"):-len(".json")] for p in glob.glob(os.path.join(GOLD, "greedy_*.json")))

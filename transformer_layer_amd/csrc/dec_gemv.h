@@ -4,7 +4,8 @@
 // streams whole 16-byte "granules" of weight rows with coalesced loads: lane
 // l of a wave reads granule (j*KS + ks)*64 + l of a row, so each load
 // instruction of the wave covers 1 KiB of contiguous weight bytes. A granule
-// is 4 fp32, 8 bf16 or 32 four-bit weights. KS waves (1 or 4) of a workgroup
+// is 4 fp32 or 8 bf16 weights (4-bit weights have their own kernel, on the
+// matrix cores). KS waves (1 or 4) of a workgroup
 // share one task's rows by splitting the columns; their partial dot products
 // meet in LDS. Each lane's dot product is reduced across the wave with DPP
 // row operations.
@@ -30,7 +31,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct WF32 { static constexpr int GE = 4; static constexpr int ID = 0; };
 struct WBF16 { static constexpr int GE = 8; static constexpr int ID = 1; };
-struct WQ4 { static constexpr int GE = 32; static constexpr int ID = 2; };
 
 enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_STORE2 = 4, EPI_NORM_STORE = 5 };
 
@@ -64,39 +64,6 @@ __device__ __forceinline__ float granule_dot<WBF16>(u32x4 w, const float* u, flo
   return acc;
 }
 
-// Byte n of a 32-bit word as a float (v_cvt_f32_ubyte<n>: one instruction,
-// no separate extract).
-__device__ __forceinline__ float ubyte0(uint32_t x) { float r; asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x)); return r; }
-__device__ __forceinline__ float ubyte1(uint32_t x) { float r; asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x)); return r; }
-__device__ __forceinline__ float ubyte2(uint32_t x) { float r; asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x)); return r; }
-__device__ __forceinline__ float ubyte3(uint32_t x) { float r; asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x)); return r; }
-
-// Four-bit granule: returns sum_e (code_e + 8) * u_e. XOR with 0x8 turns each
-// two's-complement nibble into the unsigned value code + 8; the caller
-// subtracts 8 * sum(u) and applies the block scale. Each 32-bit word holds
-// elements 8k..8k+7 (element 2i in the low nibble of byte i); the four words
-// accumulate independently and meet at the end.
-__device__ __forceinline__ float q4_dot_offset(u32x4 w, const float* u) {
-  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-  float part[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t t = words[k] ^ 0x88888888u;
-    const uint32_t lo = t & 0x0f0f0f0fu;          // elements 8k + 0, 2, 4, 6
-    const uint32_t hi = (t >> 4) & 0x0f0f0f0fu;   // elements 8k + 1, 3, 5, 7
-    float s = ubyte0(lo) * u[8 * k + 0];
-    s = fmaf(ubyte0(hi), u[8 * k + 1], s);
-    s = fmaf(ubyte1(lo), u[8 * k + 2], s);
-    s = fmaf(ubyte1(hi), u[8 * k + 3], s);
-    s = fmaf(ubyte2(lo), u[8 * k + 4], s);
-    s = fmaf(ubyte2(hi), u[8 * k + 5], s);
-    s = fmaf(ubyte3(lo), u[8 * k + 6], s);
-    s = fmaf(ubyte3(hi), u[8 * k + 7], s);
-    part[k] = s;
-  }
-  return (part[0] + part[1]) + (part[2] + part[3]);
-}
-
 // GE norm-weight values of granule gi (f32 or bf16), with 16-byte loads.
 template <int GE>
 __device__ __forceinline__ void load_norm_granule(const void* g, int ntype, int gi, float* out) {
@@ -123,6 +90,109 @@ __device__ __forceinline__ void load_norm_granule(const void* g, int ntype, int 
   }
 }
 
+// Row pairs of a projection and what is done with their two dot products.
+// Pair p is (r0, r1): a RoPE pair (i, i + d/2) of a head (QKV), a gate row
+// and an up row of the same index (gated FFN, per-op gate/up), or two
+// consecutive rows (everything else). Shared by every GEMV kernel, so a row
+// is stored the same way whichever kernel computed it.
+template <int EPI>
+struct PairEpi {
+  static constexpr bool PAIRED = (EPI == EPI_SWIGLU || EPI == EPI_STORE2);  // rows from two matrices
+  static constexpr bool CONSEC = (EPI == EPI_STORE || EPI == EPI_RESIDUAL || EPI == EPI_NORM_STORE);
+
+  static __device__ __forceinline__ int npairs(const GemvArgs& a) {
+    return CONSEC ? (a.rows + 1) / 2 : a.rows / (PAIRED ? 1 : 2);
+  }
+
+  static __device__ __forceinline__ void rows(const GemvArgs& a, int p, int& r0, int& r1) {
+    if constexpr (EPI == EPI_QKV) {
+      const int half = a.d / 2;
+      r0 = (p / half) * a.d + (p % half);
+      r1 = r0 + half;
+    } else if constexpr (PAIRED) {
+      r0 = p;
+      r1 = p;
+    } else {
+      r0 = 2 * p;
+      r1 = r0 + 1;
+    }
+  }
+
+  // inputs of pair p's epilogue that do not depend on the dot products (the
+  // residual's old x values; RoPE's cos and sin), so they can be requested
+  // before the dot products are done
+  static __device__ __forceinline__ void inputs(const GemvArgs& a, int pos, int p, float& e0, float& e1) {
+    if (p >= npairs(a)) return;
+    int r0, r1;
+    rows(a, p, r0, r1);
+    if constexpr (EPI == EPI_RESIDUAL) {
+      e0 = r0 < a.rows ? a.x[r0] : 0.0f;
+      e1 = r1 < a.rows ? a.x[r1] : 0.0f;
+    } else if constexpr (EPI == EPI_QKV) {
+      const int half = a.d / 2;
+      const int i = p % half;
+      e0 = a.rope[(size_t(pos) * half + i) * 2];
+      e1 = a.rope[(size_t(pos) * half + i) * 2 + 1];
+    }
+  }
+
+  // the epilogue of pair p (run by one lane)
+  static __device__ __forceinline__ void finish(const GemvArgs& a, int pos, int p, float y0, float y1, float e0,
+                                                float e1) {
+    if (p >= npairs(a)) return;
+    int r0, r1;
+    rows(a, p, r0, r1);
+    const bool v0 = r0 < a.rows;
+    const bool v1 = r1 < a.rows;
+    if constexpr (EPI == EPI_STORE || EPI == EPI_NORM_STORE) {
+      if (v0) a.y[r0] = y0;
+      if (v1) a.y[r1] = y1;
+    } else if constexpr (EPI == EPI_RESIDUAL) {
+      if (v0) a.x[r0] = e0 + y0;
+      if (v1) a.x[r1] = e1 + y1;
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      a.y[r0] = swiglu(y0, y1);
+    } else if constexpr (EPI == EPI_STORE2) {
+      a.y[r0] = y0;
+      a.y2[r0] = y1;
+    } else {  // EPI_QKV
+      const int half = a.d / 2;
+      const int head = p / half;
+      const int i = p % half;
+      if (head < a.nq + a.nkv) rope_rotate(y0, y1, e0, e1);
+      if (head < a.nq) {
+        a.y[r0] = y0;
+        a.y[r1] = y1;
+      } else {
+        const bool isk = head < a.nq + a.nkv;
+        const int j = isk ? head - a.nq : head - a.nq - a.nkv;
+        const size_t off = (size_t(j) * a.max_ctx + pos) * a.d + i;
+        void* cache = isk ? a.kc : a.vc;
+        if (a.kvtype == 1) {
+          uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
+          c16[off] = f32_to_bf16(y0);
+          c16[off + half] = f32_to_bf16(y1);
+        } else {
+          float* c32 = reinterpret_cast<float*>(cache);
+          c32[off] = y0;
+          c32[off + half] = y1;
+        }
+      }
+    }
+  }
+};
+
+// Position check of the QKV epilogue: the position the token is written at
+// must lie in the cache. Returns false (and flags the error once) if not.
+__device__ __forceinline__ bool qkv_pos_ok(const GemvArgs& a, int& pos) {
+  pos = *a.pos;
+  if (pos < 0 || pos >= a.max_ctx) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.err, kErrPos);
+    return false;
+  }
+  return true;
+}
+
 // One task is NP row pairs (NR = 2 NP rows): a RoPE pair (i, i + d/2) of a
 // head (QKV), a gate row and an up row (gated FFN), or two consecutive rows.
 // PF: the next task's weights are requested before the current task is
@@ -145,8 +215,8 @@ void gemv_kernel(GemvArgs a) {
   constexpr int GE = T::GE;
   constexpr int NR = 2 * NP;  // rows per task
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_NORM_STORE);
-  constexpr bool Q4 = (T::ID == 2);
-  constexpr bool PAIRED = (EPI == EPI_SWIGLU || EPI == EPI_STORE2);  // rows from two matrices
+  using PE = PairEpi<EPI>;
+  constexpr bool PAIRED = PE::PAIRED;
   constexpr int TPW = kWaves / KS;  // tasks per workgroup iteration
 
   if (a.null_kernel) return;
@@ -157,47 +227,26 @@ void gemv_kernel(GemvArgs a) {
 
   int pos = 0;
   if constexpr (EPI == EPI_QKV) {
-    pos = *a.pos;
-    if (pos < 0 || pos >= a.max_ctx) {
-      if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.err, kErrPos);
-      return;
-    }
+    if (!qkv_pos_ok(a, pos)) return;
   }
 
   const int G = a.cols / GE;  // granules per row
-  const size_t row_bytes = Q4 ? size_t(a.cols) / 2 : size_t(a.cols) * (T::ID == 0 ? 4 : 2);
-  const int half = a.d / 2;
-  constexpr bool CONSEC = (EPI == EPI_STORE || EPI == EPI_RESIDUAL || EPI == EPI_NORM_STORE);  // consecutive rows
-  const int npairs = CONSEC ? (a.rows + 1) / 2 : a.rows / (PAIRED ? 1 : 2);
+  const size_t row_bytes = size_t(a.cols) * (T::ID == 0 ? 4 : 2);
+  const int npairs = PE::npairs(a);
   const uint8_t* Wa = reinterpret_cast<const uint8_t*>(a.W);
   const uint8_t* Wb = PAIRED ? reinterpret_cast<const uint8_t*>(a.W2) : Wa;
-  const __half* Sa = reinterpret_cast<const __half*>(a.S);
-  const __half* Sb = PAIRED ? reinterpret_cast<const __half*>(a.S2) : Sa;
 
-  // rows of pair p: (r0, r1), r0 from matrix a, r1 from matrix a or b
-  auto rows_of = [&](int p, int& r0, int& r1) {
-    if constexpr (EPI == EPI_QKV) {
-      r0 = (p / half) * a.d + (p % half);
-      r1 = r0 + half;
-    } else if constexpr (PAIRED) {
-      r0 = p;
-      r1 = p;
-    } else {
-      r0 = 2 * p;
-      r1 = r0 + 1;
-    }
-  };
-  // weights (and 4-bit block scales) of a task's rows. Loads are never
+  // weights of a task's rows. Loads are never
   // predicated: a granule past the row end reads the row's last granule
   // (its input values are zero) and a row past the matrix reads the last row
   // (its result is never stored).
-  auto load_task = [&](int task, u32x4 (&wq)[NR][NJ], float (&sc)[NR][NJ]) {
+  auto load_task = [&](int task, u32x4 (&wq)[NR][NJ]) {
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       int p = task * NP + q;
       p = p < npairs ? p : npairs - 1;
       int r0, r1;
-      rows_of(p, r0, r1);
+      PE::rows(a, p, r0, r1);
       r0 = r0 < a.rows ? r0 : a.rows - 1;
       r1 = r1 < a.rows ? r1 : a.rows - 1;
 #pragma unroll
@@ -206,10 +255,6 @@ void gemv_kernel(GemvArgs a) {
         gi = gi < G ? gi : G - 1;
         wq[2 * q][j] = ldg16(Wa + size_t(r0) * row_bytes + size_t(gi) * 16);
         wq[2 * q + 1][j] = ldg16(Wb + size_t(r1) * row_bytes + size_t(gi) * 16);
-        if constexpr (Q4) {
-          sc[2 * q][j] = __half2float(Sa[size_t(r0) * G + gi]);
-          sc[2 * q + 1][j] = __half2float(Sb[size_t(r1) * G + gi]);
-        }
       }
     }
   };
@@ -218,16 +263,14 @@ void gemv_kernel(GemvArgs a) {
   // the prologue reads and normalizes the input vector
   const int stride = gridDim.x * TPW;
   u32x4 wq[NR][NJ];
-  float sc[NR][NJ];
-  load_task(blockIdx.x * TPW + slot, wq, sc);
+  load_task(blockIdx.x * TPW + slot, wq);
 
   // ---- prologue: this lane's slice of the input vector, in registers. The
   // norm weights are requested together with it when they fit in registers
   // (they do not depend on the sum of squares).
-  constexpr bool EARLY_NORM = NORM && !Q4 && NJ * GE <= 32;
+  constexpr bool EARLY_NORM = NORM && NJ * GE <= 32;
   float u[NJ][GE];
   float gw[EARLY_NORM ? NJ : 1][EARLY_NORM ? GE : 1];
-  float usum[NJ];
   float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -276,76 +319,8 @@ void gemv_kernel(GemvArgs a) {
       for (int e = 0; e < GE; ++e) u[j][e] = (u[j][e] * r) * g[e];   // u is 0 past the row end
     }
   }
-  if constexpr (Q4) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      float s = 0.0f;
-#pragma unroll
-      for (int e = 0; e < GE; ++e) s += u[j][e];
-      usum[j] = 8.0f * s;
-    }
-  }
-
-  // ---- inputs of a pair's epilogue that do not depend on the dot products
-  // (the residual's old x values; RoPE's cos and sin), requested when the
-  // task starts by the lane that will finish the pair, so no load is left
-  // for the end of the task
-  auto epi_inputs = [&](int p, float& e0, float& e1) {
-    if (p >= npairs) return;
-    int r0, r1;
-    rows_of(p, r0, r1);
-    if constexpr (EPI == EPI_RESIDUAL) {
-      e0 = r0 < a.rows ? a.x[r0] : 0.0f;
-      e1 = r1 < a.rows ? a.x[r1] : 0.0f;
-    } else if constexpr (EPI == EPI_QKV) {
-      const int i = p % half;
-      e0 = a.rope[(size_t(pos) * half + i) * 2];
-      e1 = a.rope[(size_t(pos) * half + i) * 2 + 1];
-    }
-  };
-
-  // ---- epilogue of one row pair (run by one lane)
-  auto epilogue = [&](int p, float y0, float y1, float e0, float e1) {
-    if (p >= npairs) return;
-    int r0, r1;
-    rows_of(p, r0, r1);
-    const bool v0 = r0 < a.rows;
-    const bool v1 = r1 < a.rows;
-    if constexpr (EPI == EPI_STORE || EPI == EPI_NORM_STORE) {
-      if (v0) a.y[r0] = y0;
-      if (v1) a.y[r1] = y1;
-    } else if constexpr (EPI == EPI_RESIDUAL) {
-      if (v0) a.x[r0] = e0 + y0;
-      if (v1) a.x[r1] = e1 + y1;
-    } else if constexpr (EPI == EPI_SWIGLU) {
-      a.y[r0] = swiglu(y0, y1);
-    } else if constexpr (EPI == EPI_STORE2) {
-      a.y[r0] = y0;
-      a.y2[r0] = y1;
-    } else {  // EPI_QKV
-      const int head = p / half;
-      const int i = p % half;
-      if (head < a.nq + a.nkv) rope_rotate(y0, y1, e0, e1);
-      if (head < a.nq) {
-        a.y[r0] = y0;
-        a.y[r1] = y1;
-      } else {
-        const bool isk = head < a.nq + a.nkv;
-        const int j = isk ? head - a.nq : head - a.nq - a.nkv;
-        const size_t off = (size_t(j) * a.max_ctx + pos) * a.d + i;
-        void* cache = isk ? a.kc : a.vc;
-        if (a.kvtype == 1) {
-          uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
-          c16[off] = f32_to_bf16(y0);
-          c16[off + half] = f32_to_bf16(y1);
-        } else {
-          float* c32 = reinterpret_cast<float*>(cache);
-          c32[off] = y0;
-          c32[off + half] = y1;
-        }
-      }
-    }
-  };
+  auto epi_inputs = [&](int p, float& e0, float& e1) { PE::inputs(a, pos, p, e0, e1); };
+  auto epilogue = [&](int p, float y0, float y1, float e0, float e1) { PE::finish(a, pos, p, y0, y1, e0, e1); };
 
   // ---- tasks: this wave slot handles task, task + stride, ...
   int nb = 0;                         // tasks in the current LDS batch
@@ -365,43 +340,26 @@ void gemv_kernel(GemvArgs a) {
       }
     }
     u32x4 wn[PF ? NR : 1][NJ];
-    float sn[PF ? NR : 1][NJ];
     if constexpr (PF) {
-      if (more) load_task(task + stride, wn, sn);
+      if (more) load_task(task + stride, wn);
     }
 
     float acc[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) acc[k] = 0.0f;
-    if constexpr (Q4) {
 #pragma unroll
-      for (int k = 0; k < NR; ++k)
+    for (int k = 0; k < NR; ++k)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          acc[k] = fmaf(sc[k][j], q4_dot_offset(wq[k][j], u[j]) - usum[j], acc[k]);
-          // keep each granule's conversions next to its multiply-adds (the
-          // scheduler would otherwise convert every granule first and run
-          // out of registers)
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
-#pragma unroll
-      for (int k = 0; k < NR; ++k)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[k] = granule_dot<T>(wq[k][j], u[j], acc[k]);
-    }
+      for (int j = 0; j < NJ; ++j) acc[k] = granule_dot<T>(wq[k][j], u[j], acc[k]);
     if constexpr (PF) {
       if (more) {
 #pragma unroll
         for (int k = 0; k < NR; ++k)
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            wq[k][j] = wn[k][j];
-            if constexpr (Q4) sc[k][j] = sn[k][j];
-          }
+          for (int j = 0; j < NJ; ++j) wq[k][j] = wn[k][j];
       }
     } else {
-      if (more) load_task(task + stride, wq, sc);
+      if (more) load_task(task + stride, wq);
     }
 #pragma unroll
     for (int k = 0; k < NR; ++k) acc[k] = wave_sum(acc[k]);
@@ -444,24 +402,25 @@ void gemv_kernel(GemvArgs a) {
 }
 
 // Workgroups that one kernel keeps resident on the current device
-// (occupancy x compute units), cached per (device, kernel): every GEMV
-// instantiation has its own register use and so its own occupancy.
+// (occupancy x compute units) for a block size and dynamic LDS size, cached
+// per (device, kernel, LDS size): every instantiation has its own register
+// use and so its own occupancy.
 template <class K>
-inline int resident_blocks(K kernel) {
-  struct Entry { const void* fn; int dev; int cap; };
-  static thread_local Entry cache[128];
+inline int resident_blocks(K kernel, int block = kBlock, int lds = 0) {
+  struct Entry { const void* fn; int dev; int lds; int cap; };
+  static thread_local Entry cache[256];
   static thread_local int used = 0;
   const void* fn = reinterpret_cast<const void*>(kernel);
   int dev = 0;
   (void)hipGetDevice(&dev);
   for (int i = 0; i < used; ++i)
-    if (cache[i].fn == fn && cache[i].dev == dev) return cache[i].cap;
+    if (cache[i].fn == fn && cache[i].dev == dev && cache[i].lds == lds) return cache[i].cap;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds) != hipSuccess || per_cu < 1)
     per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
   const int cap = per_cu * cus;
-  if (used < 128) cache[used++] = Entry{fn, dev, cap};
+  if (used < 256) cache[used++] = Entry{fn, dev, lds, cap};
   return cap;
 }
 

@@ -1,57 +1,54 @@
-// GEMV-core instantiations for q4 weights.
-#include "dec_gemv.h"
+// Launches of the four-bit GEMV (matrix-core kernel).
+#include "dec_q4mfma.h"
 
 namespace dec {
 
-// Row pairs per task: two when a lane holds few granules of a row, so that a
-// wave still has several 16-byte loads in flight; one otherwise (fewer
-// registers, higher occupancy). Measured on the 7B/9B layer shapes, fetching
-// the next task ahead (PF) did not help once occupancy was high.
-template <int NJ>
-constexpr int pairs_per_task() { return NJ <= 1 ? 2 : 1; }
-
-template <int NJ, int KS, int EPI>
-static hipError_t go_q4_epi(GemvArgs a, hipStream_t s) {
-  constexpr int NP = pairs_per_task<NJ>();
-  auto kernel = gemv_kernel<WQ4, NJ, KS, EPI, NP, false>;
-  a.ntask = (a.ntask + NP - 1) / NP;  // row pairs -> tasks
-  const int tpw = kWaves / KS;
-  const int groups = (a.ntask + tpw - 1) / tpw;
-  if (groups <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kernel, dim3(gemv_grid(kernel, groups)), dim3(kBlock), 0, s, a);
+template <int EPI, int NW, int SPW>
+static hipError_t go_q4mfma(const GemvArgs& a, int ntiles, hipStream_t s) {
+  // one tile per workgroup when every tile's workgroup fits on the chip at
+  // once; otherwise two adjacent tiles per workgroup
+  auto one = q4mfma_kernel<EPI, NW, SPW, 1>;
+  const int lds1 = q4mfma_lds_bytes(a.cols, NW, SPW, 1);
+  if (ntiles <= resident_blocks(one, NW * 64, lds1)) {
+    hipLaunchKernelGGL(one, dim3(ntiles), dim3(NW * 64), lds1, s, a);
+  } else {
+    auto two = q4mfma_kernel<EPI, NW, SPW, 2>;
+    hipLaunchKernelGGL(two, dim3((ntiles + 1) / 2), dim3(NW * 64), q4mfma_lds_bytes(a.cols, NW, SPW, 2), s, a);
+  }
   return hipGetLastError();
 }
 
-template <int NJ, int KS>
-static hipError_t go_q4(int epi, const GemvArgs& a, hipStream_t s) {
-  switch (epi) {
-    case kEpiStore: return go_q4_epi<NJ, KS, EPI_STORE>(a, s);
-    case kEpiResidual: return go_q4_epi<NJ, KS, EPI_RESIDUAL>(a, s);
-    case kEpiQkv: return go_q4_epi<NJ, KS, EPI_QKV>(a, s);
-    case kEpiSwiglu: return go_q4_epi<NJ, KS, EPI_SWIGLU>(a, s);
-    case kEpiStore2: return go_q4_epi<NJ, KS, EPI_STORE2>(a, s);
-    case kEpiNormStore: return go_q4_epi<NJ, KS, EPI_NORM_STORE>(a, s);
+template <int EPI, int NW>
+static hipError_t go_q4mfma_spw(const GemvArgs& a, int ntiles, int spw, hipStream_t s) {
+  switch (spw) {
+    case 4: return go_q4mfma<EPI, NW, 4>(a, ntiles, s);
+    case 8: return go_q4mfma<EPI, NW, 8>(a, ntiles, s);
+    case 12: return go_q4mfma<EPI, NW, 12>(a, ntiles, s);
+    case 16: return go_q4mfma<EPI, NW, 16>(a, ntiles, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int EPI>
+static hipError_t go_q4mfma_epi(const GemvArgs& a, hipStream_t s) {
+  // row pairs -> tiles of eight pairs
+  const int ntiles = (a.ntask + 7) / 8;
+  if (ntiles <= 0) return hipSuccess;
+  int nw = 0, spw = 0;
+  if (!q4mfma_plan(a.cols, ntiles, &nw, &spw)) return hipErrorInvalidValue;
+  return nw == 8 ? go_q4mfma_spw<EPI, 8>(a, ntiles, spw, s) : go_q4mfma_spw<EPI, 4>(a, ntiles, spw, s);
+}
+
 hipError_t launch_gemv_q4(int epi, const GemvArgs& a, hipStream_t s) {
-  constexpr int GE = 32;
-  const int ks = gemv_ks(a.cols, GE);
-  const int nj = gemv_nj(a.cols, GE, ks);
-  if (ks == 1) {
-    if (nj <= 1) return go_q4<1, 1>(epi, a, s);
-    if (nj <= 2) return go_q4<2, 1>(epi, a, s);
+  switch (epi) {
+    case kEpiStore: return go_q4mfma_epi<EPI_STORE>(a, s);
+    case kEpiResidual: return go_q4mfma_epi<EPI_RESIDUAL>(a, s);
+    case kEpiQkv: return go_q4mfma_epi<EPI_QKV>(a, s);
+    case kEpiSwiglu: return go_q4mfma_epi<EPI_SWIGLU>(a, s);
+    case kEpiStore2: return go_q4mfma_epi<EPI_STORE2>(a, s);
+    case kEpiNormStore: return go_q4mfma_epi<EPI_NORM_STORE>(a, s);
+    default: return hipErrorInvalidValue;
   }
-  if (ks == 2) {
-    if (nj <= 1) return go_q4<1, 2>(epi, a, s);
-    if (nj <= 2) return go_q4<2, 2>(epi, a, s);
-  }
-  if (ks == 4) {
-    if (nj <= 1) return go_q4<1, 4>(epi, a, s);
-    if (nj <= 2) return go_q4<2, 4>(epi, a, s);
-  }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace dec

@@ -45,15 +45,31 @@ inline int gemv_nj(int cols, int ge, int ks) {
 }
 
 // Waves that share one row (1, 2 or 4): the fewest that keep a lane's slice
-// of the input vector within `budget` registers (16 for f32/bf16 weights, 32
-// for 4-bit weights, whose granules hold 32 elements); four when none does.
-// The fused kernels and the per-op RMSNorm both follow this rule, so they
+// of the input vector within 16 registers; four when none does. The fused
+// f32/bf16 kernels and the per-op RMSNorm both follow this rule, so they
 // accumulate in the same order.
 inline int gemv_ks(int cols, int ge) {
-  const int budget = ge == 32 ? 32 : 16;
   for (int ks = 1; ks <= 4; ks *= 2)
-    if (gemv_nj(cols, ge, ks) * ge <= budget) return ks;
+    if (gemv_nj(cols, ge, ks) * ge <= 16) return ks;
   return 4;
+}
+
+// Four-bit GEMV on the matrix cores: waves per workgroup (4, or 8 when the
+// projection has few 16-row tiles, so that more waves share each tile's
+// steps of four 32-element blocks) and steps per wave (rounded up to 4, 8,
+// 12 or 16). False when a wave would need more than 16 steps (cols > 16384).
+inline bool q4mfma_plan(int cols, int ntiles, int* nw, int* spw) {
+  const int steps = (cols / 32 + 3) / 4;
+  int w = ntiles < 1024 ? 8 : 4;
+  int per = (steps + w - 1) / w;
+  if (per > 16 && w == 4) {
+    w = 8;
+    per = (steps + w - 1) / w;
+  }
+  if (per > 16) return false;
+  *nw = w;
+  *spw = per <= 4 ? 4 : per <= 8 ? 8 : per <= 12 ? 12 : 16;
+  return true;
 }
 
 enum GemvEpi { kEpiStore = 0, kEpiResidual = 1, kEpiQkv = 2, kEpiSwiglu = 3, kEpiStore2 = 4, kEpiNormStore = 5 };

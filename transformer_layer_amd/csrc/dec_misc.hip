@@ -2,13 +2,15 @@
 // the per-token embedding gather and position advance.
 #include "dec_device.h"
 #include "dec_internal.h"
+#include "dec_q4mfma.h"
 
 namespace dec {
 
 // RMSNorm of x (optionally times the norm weight) into `out`, one workgroup.
-// The sum of squares is accumulated in the same lane order as the GEMV
-// prologue of the fused kernels (granules of `ge` elements, `ks` waves per
-// row), so the per-op path rounds exactly like the fused one.
+// The sum of squares is accumulated in the same lane order as the prologue
+// of the fused kernels for the same weight type (f32/bf16: granules of `ge`
+// elements, `ks` waves per row; 4-bit: the matrix-core kernel's order), so
+// the per-op path rounds exactly like the fused one.
 __global__ __launch_bounds__(kBlock) void rmsnorm_kernel(const float* x, const void* g, int ntype,
                                                          float* out, int n, float eps, int ge,
                                                          int ks, int with_weight, int null_kernel) {
@@ -17,20 +19,26 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_kernel(const float* x, const v
   __shared__ float rs;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
-  const int G = n / ge;
-  if (wv < ks) {
-    float ss = 0.0f;
-    for (int j = 0;; ++j) {
-      const int gi = (j * ks + wv) * kWave + lane;
-      if ((j * ks + wv) * kWave >= G) break;
-      if (gi < G)
-        for (int e = 0; e < ge; ++e) {
-          const float v = x[gi * ge + e];
-          ss = fmaf(v, v, ss);
-        }
-    }
-    ss = wave_sum(ss);
+  if (ge == 32) {
+    const float ss = q4mfma_sumsq_part(reinterpret_cast<const float4*>(x), n / 4, threadIdx.x);
     if (lane == 0) ssq[wv] = ss;
+    ks = kWaves;
+  } else {
+    const int G = n / ge;
+    if (wv < ks) {
+      float ss = 0.0f;
+      for (int j = 0;; ++j) {
+        const int gi = (j * ks + wv) * kWave + lane;
+        if ((j * ks + wv) * kWave >= G) break;
+        if (gi < G)
+          for (int e = 0; e < ge; ++e) {
+            const float v = x[gi * ge + e];
+            ss = fmaf(v, v, ss);
+          }
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) ssq[wv] = ss;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
