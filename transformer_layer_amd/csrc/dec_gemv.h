@@ -326,22 +326,39 @@ void gemv_kernel(GemvArgs a) {
   int nb = 0;                         // tasks in the current LDS batch
   int batch_base = blockIdx.x * TPW;  // base of its first task
   constexpr bool EPI_IN = (EPI == EPI_RESIDUAL || EPI == EPI_QKV);
-  float ex0 = 0.0f, ex1 = 0.0f;       // epilogue inputs of the pair this lane finishes
+  // Epilogue inputs of the pair this lane finishes (ex) and of the next
+  // task's (exn). They are requested one task ahead, together with that
+  // task's weights, so the wait for the weights covers them: requested at
+  // the start of their own task, the wait for the weights right after would
+  // wait for them too, an L2 round trip per task.
+  float ex0 = 0.0f, ex1 = 0.0f, exn0 = 0.0f, exn1 = 0.0f;
+  // the lane that finishes pair q of task t (batch item bi) requests its inputs
+  auto epi_request = [&](int t, int bi) {
+    if constexpr (KS == 1) {
+      if (lane < NP && t < a.ntask) epi_inputs(t * NP + lane, exn0, exn1);
+    } else {
+      const int q = lane - bi * NP;
+      if (ks == 0 && q >= 0 && q < NP && t < a.ntask) epi_inputs(t * NP + q, exn0, exn1);
+    }
+  };
+  if constexpr (EPI_IN) epi_request(blockIdx.x * TPW + slot, 0);
   for (int base = blockIdx.x * TPW; base < a.ntask; base += stride) {
     const int task = base + slot;
     const bool more = base + stride < a.ntask;
+    // a lane's exn holds the inputs of the batch item it finishes next; for
+    // every other lane exn and ex are already equal
     if constexpr (EPI_IN) {
-      if constexpr (KS == 1) {
-        if (lane < NP && task < a.ntask) epi_inputs(task * NP + lane, ex0, ex1);
-      } else {
-        // lane nb*NP + q of wave ks == 0 finishes pair q of this task (batch item nb)
-        const int q = lane - nb * NP;
-        if (ks == 0 && q >= 0 && q < NP && task < a.ntask) epi_inputs(task * NP + q, ex0, ex1);
-      }
+      ex0 = exn0;
+      ex1 = exn1;
     }
+    // batch item of the next task (KS > 1: a batch is finished after kBatch tasks)
+    const int nb_next = (KS > 1 && nb + 1 == kBatch) ? 0 : nb + 1;
     u32x4 wn[PF ? NR : 1][NJ];
     if constexpr (PF) {
-      if (more) load_task(task + stride, wn);
+      if (more) {
+        load_task(task + stride, wn);
+        if constexpr (EPI_IN) epi_request(task + stride, nb_next);
+      }
     }
 
     float acc[NR];
@@ -359,7 +376,10 @@ void gemv_kernel(GemvArgs a) {
           for (int j = 0; j < NJ; ++j) wq[k][j] = wn[k][j];
       }
     } else {
-      if (more) load_task(task + stride, wq);
+      if (more) {
+        load_task(task + stride, wq);
+        if constexpr (EPI_IN) epi_request(task + stride, nb_next);
+      }
     }
 #pragma unroll
     for (int k = 0; k < NR; ++k) acc[k] = wave_sum(acc[k]);
