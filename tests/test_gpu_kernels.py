@@ -129,18 +129,20 @@ def test_gemv_residual(gpu, wtype, rows, cols):
 
 
 FFN_CASES = [
-    ("f32", 256, 1024),
-    ("bf16", 2176, 1000),
-    ("bf16", 4096, 12288),
-    ("bf16", 8192, 640),
-    ("q4", 4096, 12288),
-    ("q4", 2080, 352),
+    ("f32", 256, 1024, None),
+    ("bf16", 2176, 1000, None),
+    ("bf16", 4096, 12288, None),
+    ("bf16", 8192, 640, None),
+    ("q4", 4096, 12288, None),
+    ("q4", 2080, 352, None),
+    ("q4", 2080, 352, "f32"),     # 4-bit weights with fp32 norm weights
+    ("q4", 16384, 96, None),      # the longest rows the interface allows
 ]
 
 
-@pytest.mark.parametrize("wtype,H,F", FFN_CASES)
-def test_gated_ffn(gpu, wtype, H, F):
-    cfg = _cfg(wtype, "bf16", H, 4, 4, 64, F=F)
+@pytest.mark.parametrize("wtype,H,F,ntype", FFN_CASES)
+def test_gated_ffn(gpu, wtype, H, F, ntype):
+    cfg = _cfg(wtype, "bf16", H, 4, 4, 64, F=F, ntype=ntype)
     st = DecodeStack(cfg, n_layers=1)
     g = synth.rand_norm((7, 1, H), H, cfg.ntype)
     Wg = synth.rand_matrix((7, 2, F), F, H, wtype)
@@ -211,3 +213,38 @@ def test_position_out_of_range_sets_error_and_stores_nothing(gpu):
         assert st.check_err() & L.DEC_ERR_POS
     assert bool(torch.all(st.K == SENT16)) and bool(torch.all(st.V == SENT16))
     assert bool(torch.all(st.q == 7.0))
+
+
+HEAD_CASES = [
+    # head type, H, vocab
+    ("f32", 256, 1000),
+    ("bf16", 2048, 32000),
+    ("q4", 4096, 32000),
+    ("q4", 2080, 999),            # ragged: 65 blocks per row, odd row count
+]
+
+
+@pytest.mark.parametrize("htype,H,vocab", HEAD_CASES)
+def test_lm_head_logits_and_argmax(gpu, htype, H, vocab):
+    """Final RMSNorm, head GEMV and the greedy argmax into the device token."""
+    cfg = _cfg("f32" if htype == "f32" else "bf16", "bf16", H, 4, 4, 64).with_(vocab=vocab)
+    st = DecodeStack(cfg, n_layers=1)
+    g = synth.rand_norm((8, 1, H), H, cfg.ntype)
+    head = synth.rand_matrix((8, 2, vocab), vocab, H, htype)
+    x = synth.rand_f32((8, 3, H), (H,))
+    st.set_head(g, head)
+    st.x.copy_(torch.from_numpy(x))
+    st.token.fill_(-1)
+    st.head_step()
+    torch.cuda.synchronize()
+    xf = oracle.rmsnorm(x.astype(np.float64), oracle.dequant(g), cfg.rms_eps)
+    ref = oracle.gemv(oracle.dequant(head), xf)
+    got = st.logits.cpu().numpy()
+    assert rel_l2(got, ref) <= TOL
+    # the token is the argmax of the logits the kernel wrote (lowest index on
+    # ties), and the oracle's own argmax unless its top two are within the error
+    tok = int(st.token.item())
+    assert tok == int(np.argmax(got))
+    top2 = np.sort(ref)[-2:]
+    if top2[1] - top2[0] > 1e-4 * np.abs(ref).max():
+        assert tok == int(np.argmax(ref))

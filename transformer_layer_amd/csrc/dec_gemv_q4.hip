@@ -9,11 +9,13 @@ static hipError_t go_q4mfma(const GemvArgs& a, int ntiles, hipStream_t s) {
   // once; otherwise two adjacent tiles per workgroup
   auto one = q4mfma_kernel<EPI, NW, SPW, 1>;
   const int lds1 = q4mfma_lds_bytes(a.cols, NW, SPW, 1);
-  if (ntiles <= resident_blocks(one, NW * 64, lds1)) {
+  const int lds2 = q4mfma_lds_bytes(a.cols, NW, SPW, 2);
+  if (lds1 > 65536) return hipErrorInvalidValue;
+  if (ntiles <= resident_blocks(one, NW * 64, lds1) || lds2 > 65536) {
     hipLaunchKernelGGL(one, dim3(ntiles), dim3(NW * 64), lds1, s, a);
   } else {
     auto two = q4mfma_kernel<EPI, NW, SPW, 2>;
-    hipLaunchKernelGGL(two, dim3((ntiles + 1) / 2), dim3(NW * 64), q4mfma_lds_bytes(a.cols, NW, SPW, 2), s, a);
+    hipLaunchKernelGGL(two, dim3((ntiles + 1) / 2), dim3(NW * 64), lds2, s, a);
   }
   return hipGetLastError();
 }

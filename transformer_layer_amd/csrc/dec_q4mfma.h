@@ -41,12 +41,19 @@ namespace dec {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
+// Block scales go through LDS for up to 12 steps per wave; for the longest
+// rows (16 steps, up to 16384 columns) that would pass 64 KB, and each lane
+// loads its own scales instead.
+__host__ __device__ constexpr bool q4mfma_scales_in_lds(int spw) { return spw <= 12; }
+
 // LDS bytes: the digits and exponents of `cols` elements (blocks padded to a
 // whole step), the cross-wave sums (double-buffered), the sum-of-squares
-// slots, 16 zero bytes, and every wave's block scales of its tiles
-// ([nw][tt][16 rows][4 spw blocks] fp16).
+// slots, 16 zero bytes, and (scales in LDS) every wave's block scales of its
+// tiles ([nw][tt][16 rows][4 spw blocks] fp16). At most 64 KB for every
+// shape the launcher accepts (64032 bytes at 12288 columns, two tiles).
 __host__ __device__ constexpr int q4mfma_lds_bytes(int cols, int nw, int spw, int tt) {
-  return ((cols / 32 + 3) / 4) * 4 * (96 + 4) + nw * 16 * 4 * 2 + 16 + 16 + nw * tt * 16 * 4 * spw * 2;
+  return ((cols / 32 + 3) / 4) * 4 * (96 + 4) + nw * 16 * 4 * 2 + 16 + 16 +
+         (q4mfma_scales_in_lds(spw) ? nw * tt * 16 * 4 * spw * 2 : 0);
 }
 
 // Sum of squares of the input vector in the order the 4-bit kernels use
@@ -253,22 +260,36 @@ __global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
     }
   };
   // block scales of this wave's steps (4 SPW blocks from block 4 s0) for the
-  // tile's 16 rows, with row-contiguous 2-byte loads (KL lanes per row, so a
-  // load touches few cache lines); they go to LDS and each step reads its
-  // lane's scale there
+  // tile's 16 rows. In LDS mode: row-contiguous 2-byte loads (KL lanes per
+  // row, so a load touches few cache lines) written to LDS, where each step
+  // reads its lane's scale. Otherwise each lane loads the scale of each of
+  // its steps (a 32-bit register per scale: two 16-bit values packed in one
+  // register would make each load wait for the previous one).
+  constexpr bool SL = q4mfma_scales_in_lds(SPW);
   constexpr int KB = 4 * SPW;                       // blocks per row of a wave's share
   constexpr int KL = KB <= 16 ? 16 : KB <= 32 ? 32 : 64;   // lanes per row in a load
-  constexpr int NSL = 16 * KL / 64;                 // scale loads per tile
+  constexpr int NSL = SL ? 16 * KL / 64 : SPW;      // scale loads per tile
   uint32_t sv[TT][NSL];
   auto load_scales = [&](int tile, uint32_t (&v)[NSL]) {
+    if constexpr (SL) {
 #pragma unroll
-    for (int k = 0; k < NSL; ++k) {
-      const int rr = k * (64 / KL) + lane / KL;   // row of the tile
+      for (int k = 0; k < NSL; ++k) {
+        const int rr = k * (64 / KL) + lane / KL;   // row of the tile
+        bool second;
+        const int r = row_at(tile, rr, second);
+        int b = 4 * s0 + lane % KL;
+        b = b < G ? b : G - 1;
+        v[k] = reinterpret_cast<const uint16_t*>(second ? a.S2 : a.S)[size_t(r) * G + b];
+      }
+    } else {
       bool second;
-      const int r = row_at(tile, rr, second);
-      int b = 4 * s0 + lane % KL;
-      b = b < G ? b : G - 1;
-      v[k] = reinterpret_cast<const uint16_t*>(second ? a.S2 : a.S)[size_t(r) * G + b];
+      const int r = row_at(tile, n, second);
+#pragma unroll
+      for (int i = 0; i < SPW; ++i) {
+        int b = 4 * (s0 + i) + g;
+        b = b < G ? b : G - 1;
+        v[i] = reinterpret_cast<const uint16_t*>(second ? a.S2 : a.S)[size_t(r) * G + b];
+      }
     }
   };
   uint16_t* scl = reinterpret_cast<uint16_t*>(zero16 + 16) + wv * TT * 16 * KB;   // [TT][16][KB]
@@ -315,14 +336,16 @@ __global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
     else
       q4mfma_quantize<true, 0, GQ>(a, r, xv, gv, dig, ex, GP, tid);
   }
+  if constexpr (SL) {
 #pragma unroll
-  for (int t = 0; t < TT; ++t)
+    for (int t = 0; t < TT; ++t)
 #pragma unroll
-    for (int k = 0; k < NSL; ++k) {
-      const int rr = k * (64 / KL) + lane / KL;
-      const int j = lane % KL;
-      if (j < KB) scl[(t * 16 + rr) * KB + j] = uint16_t(sv[t][k]);
-    }
+      for (int k = 0; k < NSL; ++k) {
+        const int rr = k * (64 / KL) + lane / KL;
+        const int j = lane % KL;
+        if (j < KB) scl[(t * 16 + rr) * KB + j] = uint16_t(sv[t][k]);
+      }
+  }
   __syncthreads();
 
   // the digit operand of this lane: block 4 s + g, digit p = n % 4 when
@@ -334,8 +357,8 @@ __global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
   const int ahalf = has_a ? 16 : 0;
   const int* exl = ex + 4 * s0 + g;
 
-  auto run_tile = [&](int tile, int iter, const u32x4 (&w)[SPW]) {
-    const uint16_t* sl = scl + (iter * 16 + n) * KB + g;   // step i: block 4 i + g of row n
+  auto run_tile = [&](int tile, int iter, const u32x4 (&w)[SPW], const uint32_t (&sr)[NSL]) {
+    const uint16_t* sl = scl + (iter * 16 + n) * KB + g;   // LDS mode, step i: block 4 i + g of row n
     float e0 = 0.0f, e1 = 0.0f;
     if (wv == 0 && lane < 8) PE::inputs(a, pos, tile * 8 + lane, e0, e1);
     float acc = 0.0f;
@@ -353,7 +376,8 @@ __global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
         C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, C, 0, 0, 0);
         C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, C, 0, 0, 0);
         const float V = fmaf(float(C.z), 65536.0f, fmaf(float(C.y), 256.0f, float(C.x)));
-        acc = fmaf(ldexpf(__half2float(__ushort_as_half(sl[4 * i])), -E - 4), V, acc);
+        const uint16_t sbits = SL ? sl[4 * i] : uint16_t(sr[SL ? 0 : i]);
+        acc = fmaf(ldexpf(__half2float(__ushort_as_half(sbits)), -E - 4), V, acc);
       }
     }
     // the four k-groups of row n, then the waves
@@ -375,7 +399,7 @@ __global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
   // tiles' weights in flight; a buffer is refilled with the tile after next
   // as soon as its tile is done
 #pragma unroll
-  for (int t = 0; t < TT; ++t) run_tile(tile0 + t, t, wq[t]);
+  for (int t = 0; t < TT; ++t) run_tile(tile0 + t, t, wq[t], sv[t]);
 }
 
 }  // namespace dec
