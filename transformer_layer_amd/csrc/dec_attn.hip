@@ -6,8 +6,13 @@
 // reads its chunk of K once to score every query head of its kv head (scores
 // kept in LDS, in log2 units), turns them into exp2(s - m) with one
 // exponential per (head, position), reads the same chunk of V once, and
-// writes the split's partials: o (unnormalized) and (m, l). The first batch
-// of V rows is requested right after the K rows.
+// writes the split's partials: o (unnormalized) and (m, l). When a
+// workgroup has several row steps, its first batch of V rows is requested
+// once the scores are done (VLATE): with every workgroup's K and V requests
+// in the memory queues together, K arrived later (measured: 0.9 µs on the
+// 9B-shaped bf16 layer, 2.6 µs at 8192 positions), while V now streams
+// during the softmax. With a single row step the scores are too short to
+// cover V's latency, and V is requested right after K.
 //
 // The last workgroups of a kv head to arrive (one per ~8 KB of partials, at
 // most kCombiners) combine its partials with a log-sum-exp rescale, each a
@@ -60,7 +65,7 @@ __device__ __forceinline__ float2 load_pair_agent(const float* p) {
   return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
 }
 
-template <int D, int KVT, int G, int NW>
+template <int D, int KVT, int G, int NW, bool VLATE>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int kWaves = NW;        // waves per workgroup (4 or 8)
   constexpr int kBlock = NW * 64;
@@ -98,21 +103,24 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const u32x4 z = {0u, 0u, 0u, 0u};
   auto row = [&](int step) { return t0 + step * RPS + wv * RPW + sub; };
 
-  // first batch of K rows, then of V rows (the scores need only K, so they
-  // start while V is still arriving), then the queries
+  // first batch of K rows, of V rows (VLATE: once the scores are done),
+  // then the queries
   u32x4 kv[U], vv[U];
+  auto first_v = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = row(u);
+      const bool ok = u < nsteps && t < t1;
+      vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
+    }
+  };
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int t = row(u);
     const bool ok = u < nsteps && t < t1;
     kv[u] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + d0) * EB) : z;
   }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int t = row(u);
-    const bool ok = u < nsteps && t < t1;
-    vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
-  }
+  if constexpr (!VLATE) first_v();
   const float qscale = kLog2e / sqrtf(float(D));
   float qv[G][DPL];
 #pragma unroll
@@ -155,6 +163,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       }
     }
   }
+  if constexpr (VLATE) first_v();
   __syncthreads();
 
   // ---- per head: m = max s, p = exp2(s - m), l = sum p (one exponential per entry)
@@ -388,24 +397,32 @@ void attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chu
   *waves = nw;
 }
 
-template <int D, int KVT, int NW>
+template <int D, int KVT, int NW, bool VL>
 static hipError_t go_attn(const AttnArgs& a, hipStream_t s) {
   const int g = a.nq / a.nkv;
   const dim3 grid(a.nkv * a.nsplit), block(NW * 64);
   switch (g) {
-    case 1: hipLaunchKernelGGL((attn_kernel<D, KVT, 1, NW>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_kernel<D, KVT, 2, NW>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_kernel<D, KVT, 4, NW>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_kernel<D, KVT, 8, NW>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((attn_kernel<D, KVT, 1, NW, VL>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_kernel<D, KVT, 2, NW, VL>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_kernel<D, KVT, 4, NW, VL>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((attn_kernel<D, KVT, 8, NW, VL>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// V requested after the scores when a workgroup has more than one row step
+// (rows per step: 64 / lanes-per-row rows per wave, times the waves)
+template <int D, int KVT, int NW>
+static hipError_t go_attn_vl(const AttnArgs& a, hipStream_t s) {
+  constexpr int rows_per_step = (kWave / (D * (KVT == 1 ? 2 : 4) / 16)) * NW;
+  return a.chunk > rows_per_step ? go_attn<D, KVT, NW, true>(a, s) : go_attn<D, KVT, NW, false>(a, s);
+}
+
 template <int D, int KVT>
 static hipError_t go_attn_waves(const AttnArgs& a, hipStream_t s) {
-  if (a.waves == 8) return go_attn<D, KVT, 8>(a, s);
-  if (a.waves == 4) return go_attn<D, KVT, 4>(a, s);
+  if (a.waves == 8) return go_attn_vl<D, KVT, 8>(a, s);
+  if (a.waves == 4) return go_attn_vl<D, KVT, 4>(a, s);
   return hipErrorInvalidValue;
 }
 
