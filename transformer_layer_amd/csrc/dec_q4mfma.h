@@ -29,10 +29,10 @@
 // first tile, and quantizes the input (its first four waves) while those
 // stream in; a second tile's weights are requested once the input is
 // quantized (measured: requested together with the first, they delayed it
-// by about 0.9 µs on the 9B-shaped gated FFN). It then works through tiles of 8 row pairs (16 rows, one per
-// MFMA column); its waves split a tile's steps. A workgroup takes TT
-// adjacent tiles (one, or two when one per workgroup would not fit on the
-// chip at once). Partial sums meet across the four k-groups with lane swaps
+// by about 0.9 µs on the 9B-shaped gated FFN). A tile is 8 row pairs (16
+// rows, one per MFMA column); the waves split a tile's steps. A workgroup
+// takes TT adjacent tiles (one, or two when one per workgroup would not fit
+// on the chip at once). Partial sums meet across the four k-groups with lane swaps
 // and across waves in LDS, in a fixed order.
 #pragma once
 
