@@ -18,7 +18,7 @@ static hipError_t go_f32_epi(GemvArgs a, hipStream_t s) {
   const int tpw = kWaves / KS;
   const int groups = (a.ntask + tpw - 1) / tpw;
   if (groups <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kernel, dim3(gemv_grid(kernel, groups)), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(kernel, dim3(gemv_grid(kernel, groups, gemv_per_cu<EPI>(a.cols))), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
