@@ -132,6 +132,55 @@ def calib_copy(mb: int) -> None:
     log(f"calibration kernel: {mb} MiB read + {mb} MiB written, 3 times")
 
 
+def head_timing(st, cfg, lo: int, hi: int, steps: int, warmup: int) -> dict:
+    """The token with the LM head: final RMSNorm, head GEMV and greedy argmax
+    into the device token, which the next token's embedding reads (no
+    teacher forcing), replayed from one graph. Also the head alone (GEMV +
+    argmax, two kernels) timed back to back with HIP events on its stream.
+    The head's bytes (vocab x hidden weights + norm) are not part of the
+    stack's bytes per token."""
+    import torch
+    import synth
+
+    glob_w = synth.model_globals(cfg)
+    st.set_head(glob_w["final_norm"], glob_w["head"])
+    toks = synth.tokens(cfg, 1)
+    st.set_pos(lo)
+    st.set_token(int(toks[0]))
+    g = st.capture(lo, hi, greedy=True)
+    st.set_pos(lo)
+    st.set_token(int(toks[0]))
+    for _ in range(warmup):
+        g.replay()
+    st.set_pos(lo)
+    st.set_token(int(toks[0]))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    reps = 50
+    st.head_step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        st.head_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    head_us = e0.elapsed_time(e1) * 1e3 / reps
+    hb = synth.head_bytes(cfg)
+    log(f"with head: {1e3 / ms:.1f} tok/s, {ms:.3f} ms/token; head alone {head_us:.1f} us "
+        f"({hb / head_us / 1e3:.0f} GB/s)")
+    return {"tok_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 4), "head_us": round(head_us, 2),
+            "head_bytes": int(hb), "head_gbs": round(hb / head_us / 1e3, 1), "vocab": cfg.vocab,
+            "head_weights": glob_w["head"].kind, "kernels": 2}
+
+
 def cpu_baseline(cfg, budget_s: float = 15.0):
     """The oracle (NumPy, float64) on a bounded sample: the first layers of
     the same stack for one decode token at the first decode position, scaled
@@ -181,6 +230,7 @@ def main() -> int:
     ap.add_argument("--null-kernels", action="store_true")
     ap.add_argument("--attn-chunk", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-head", action="store_true", help="skip the greedy (LM head) timing")
     ap.add_argument("--ffn-reps", type=int, default=4,
                     help="back-to-back sweeps over the layers when timing the gated-FFN kernel")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -240,6 +290,10 @@ def main() -> int:
     gbs = bpt * tok_s / 1e9
     log(f"{tok_s:.1f} tok/s, {ms / args.steps:.3f} ms/token, {gbs:.0f} GB/s")
 
+    head = None
+    if not args.null_kernels and not args.no_head:
+        head = head_timing(st, cfg, lo, hi, args.steps, args.warmup)
+
     roof = None
     if not args.null_kernels:
         reset()
@@ -288,6 +342,7 @@ def main() -> int:
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "with_head": head,
     }
     print(json.dumps(out), flush=True)
     return 0

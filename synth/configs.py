@@ -93,6 +93,12 @@ def kv_bytes(c: DecodeConfig, length: int) -> dict:
             "write": 2 * c.n_kv_heads * c.head_dim * e}
 
 
+def head_bytes(c: DecodeConfig) -> float:
+    """Algorithmic HBM bytes of the LM head step: the head's weights
+    ``[vocab, H]`` and the final norm weight (logits and x excluded)."""
+    return c.vocab * c.hidden * elem_bytes(c.htype) + c.hidden * elem_bytes(c.ntype)
+
+
 def token_bytes(c: DecodeConfig) -> float:
     """Algorithmic HBM bytes of one decode token of the layer stack.
 

@@ -64,3 +64,11 @@ def test_traffic_summary_is_used_only_for_its_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic(cfg) == 201771210
     path.write_text("hbm_bytes_per_launch: 201771210\nkernel_source_sha256_16: 0000000000000000\n")
     assert bench.measured_traffic(cfg) is None                      # sources changed since
+
+
+@pytest.mark.parametrize("name,hbytes,nbytes", [("C1", 4, 4), ("C2", 2, 2), ("C4", 2, 2), ("C5", 2, 2)])
+def test_head_bytes_by_hand(name, hbytes, nbytes):
+    """The LM head step reads the [vocab, hidden] head (bf16 also for the
+    4-bit workload) and the final norm weight."""
+    c = synth.CONFIGS[name]
+    assert synth.head_bytes(c) == c.vocab * c.hidden * hbytes + c.hidden * nbytes
