@@ -225,11 +225,6 @@ void gemv_kernel(GemvArgs a) {
   const int ks = wv % KS;
   const int slot = wv / KS;
 
-  int pos = 0;
-  if constexpr (EPI == EPI_QKV) {
-    if (!qkv_pos_ok(a, pos)) return;
-  }
-
   const int G = a.cols / GE;  // granules per row
   const size_t row_bytes = size_t(a.cols) * (T::ID == 0 ? 4 : 2);
   const int npairs = PE::npairs(a);
@@ -265,12 +260,21 @@ void gemv_kernel(GemvArgs a) {
   u32x4 wq[NR][NJ];
   load_task(blockIdx.x * TPW + slot, wq);
 
+
   // ---- prologue: this lane's slice of the input vector, in registers. The
   // norm weights are requested together with it when they fit in registers
   // (they do not depend on the sum of squares).
+  // With bf16 weights the norm weights arrive as raw bits (16 bytes of bf16
+  // or 32 bytes of f32 per granule) from unconditional loads and are
+  // converted after the sum of squares: converted at the load, inside a
+  // branch on their type, each granule made the compiler wait for every load
+  // in flight (the first task's weights included) before the next input
+  // granule was requested.
   constexpr bool EARLY_NORM = NORM && NJ * GE <= 32;
+  constexpr bool RAW_NORM = EARLY_NORM && GE == 8;
   float u[NJ][GE];
-  float gw[EARLY_NORM ? NJ : 1][EARLY_NORM ? GE : 1];
+  float gw[EARLY_NORM && !RAW_NORM ? NJ : 1][EARLY_NORM && !RAW_NORM ? GE : 1];
+  u32x4 nr[RAW_NORM ? NJ : 1][2];
   float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -283,7 +287,15 @@ void gemv_kernel(GemvArgs a) {
       u[j][e] = ok ? v.x : 0.0f; u[j][e + 1] = ok ? v.y : 0.0f;
       u[j][e + 2] = ok ? v.z : 0.0f; u[j][e + 3] = ok ? v.w : 0.0f;
     }
-    if constexpr (EARLY_NORM) load_norm_granule<GE>(a.norm, a.ntype, gc, gw[j]);
+    if constexpr (RAW_NORM) {
+      const uint8_t* nb = reinterpret_cast<const uint8_t*>(a.norm);
+      const bool bf = a.ntype == 1;
+      const size_t o0 = size_t(gc) * (bf ? 16 : 32);
+      nr[j][0] = *reinterpret_cast<const u32x4*>(nb + o0);
+      nr[j][1] = *reinterpret_cast<const u32x4*>(nb + o0 + (bf ? 0 : 16));
+    } else if constexpr (EARLY_NORM) {
+      load_norm_granule<GE>(a.norm, a.ntype, gc, gw[j]);
+    }
   }
   if constexpr (NORM) {
 #pragma unroll
@@ -309,7 +321,18 @@ void gemv_kernel(GemvArgs a) {
     for (int j = 0; j < NJ; ++j) {
       const int gi = (j * KS + ks) * kWave + lane;
       float g[GE];
-      if constexpr (EARLY_NORM) {
+      if constexpr (RAW_NORM) {
+        const u32x4 w0 = nr[j][0], w1 = nr[j][1];
+        if (a.ntype == 1) {
+          g[0] = bf_lo(w0.x); g[1] = bf_hi(w0.x); g[2] = bf_lo(w0.y); g[3] = bf_hi(w0.y);
+          g[4] = bf_lo(w0.z); g[5] = bf_hi(w0.z); g[6] = bf_lo(w0.w); g[7] = bf_hi(w0.w);
+        } else {
+          g[0] = __uint_as_float(w0.x); g[1] = __uint_as_float(w0.y);
+          g[2] = __uint_as_float(w0.z); g[3] = __uint_as_float(w0.w);
+          g[4] = __uint_as_float(w1.x); g[5] = __uint_as_float(w1.y);
+          g[6] = __uint_as_float(w1.z); g[7] = __uint_as_float(w1.w);
+        }
+      } else if constexpr (EARLY_NORM) {
 #pragma unroll
         for (int e = 0; e < GE; ++e) g[e] = gw[j][e];
       } else {
@@ -318,6 +341,13 @@ void gemv_kernel(GemvArgs a) {
 #pragma unroll
       for (int e = 0; e < GE; ++e) u[j][e] = (u[j][e] * r) * g[e];   // u is 0 past the row end
     }
+  }
+  // the position (QKV epilogue) is checked once the first task's weights and
+  // the input slice are requested: read first, its round trip delayed every
+  // load of the workgroup
+  int pos = 0;
+  if constexpr (EPI == EPI_QKV) {
+    if (!qkv_pos_ok(a, pos)) return;
   }
   auto epi_inputs = [&](int p, float& e0, float& e1) { PE::inputs(a, pos, p, e0, e1); };
   auto epilogue = [&](int p, float y0, float y1, float e0, float e1) { PE::finish(a, pos, p, y0, y1, e0, e1); };
