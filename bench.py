@@ -60,32 +60,44 @@ def build_stack(cfg, flags, chunk):
 
 def ffn_kernel_time(st, cfg, reps: int):
     """Average duration of one gated-FFN launch, from HIP events on the
-    stream the kernel runs on: the kernel is launched for every layer of the
-    stack back to back (each layer's own weights, so nothing stays cached),
-    `reps` times, between one pair of events; the average therefore includes
-    the steady-state boundary between consecutive launches."""
+    stream the kernels run on. The kernel is launched for every layer of the
+    stack back to back (each layer's own weights, so nothing stays cached);
+    that sweep is captured once into a HIP graph, as the decode step launches
+    its kernels, and replayed `reps` times between one pair of events, so the
+    average includes the steady-state boundary between consecutive launches.
+    Returns (graph-replayed seconds per launch, launches timed, host-launched
+    seconds per launch): the same sweep launched from the host one kernel at a
+    time, for comparison (it also pays each launch's host-side submission)."""
     import torch
     from transformer_layer_amd import lib as L
 
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
+    n = reps * cfg.n_layers
 
-    def sweep():
+    def sweep(sp):
         for l in range(cfg.n_layers):
             w, s = st.wstruct[l], st.state[l]
             L.dec_gated_ffn(st.desc, w.ffn_norm, w.wgate, w.wup, s.x, s.h, sp)
 
-    sweep()
+    def timed(run):
+        stream = torch.cuda.current_stream()
+        run()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n
+
+    t_host = timed(lambda: sweep(torch.cuda.current_stream().cuda_stream))
+    g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        sweep()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    n = reps * cfg.n_layers
-    return e0.elapsed_time(e1) * 1e-3 / n, n
+    with torch.cuda.graph(g):
+        sweep(torch.cuda.current_stream().cuda_stream)
+    t_graph = timed(g.replay)
+    return t_graph, n, t_host
 
 
 def ffn_source_hash() -> str:
@@ -297,14 +309,15 @@ def main() -> int:
     roof = None
     if not args.null_kernels:
         reset()
-        t_ffn, n_ffn = ffn_kernel_time(st, cfg, args.ffn_reps)
+        t_ffn, n_ffn, t_ffn_host = ffn_kernel_time(st, cfg, args.ffn_reps)
         ffn_bytes = synth.layer_weight_bytes(cfg)["ffn"]
         ach = ffn_bytes / t_ffn / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(cfg),
                 "kernel": "dec_gated_ffn (RMSNorm + gate/up GEMV + SwiGLU)",
                 "bytes_per_launch": int(ffn_bytes), "launches_timed": n_ffn,
-                "avg_launch_us": round(t_ffn * 1e6, 2)}
+                "avg_launch_us": round(t_ffn * 1e6, 2), "timing": "graph-replayed sweep, HIP events",
+                "host_launched_avg_us": round(t_ffn_host * 1e6, 2)}
         log(f"gated FFN: {t_ffn * 1e6:.1f} us/launch, {ach:.0f} GB/s")
 
     if args.calib_copy:
