@@ -82,6 +82,10 @@ enum dec_status {
 /* dec_layer_desc.flags */
 #define DEC_UNFUSED 0x1u       /* dec_layer_step runs the ten per-op kernels */
 #define DEC_NULL_KERNELS 0x2u  /* same launches, every kernel body returns at once */
+#define DEC_TEST_NO_WAIT 0x100u /* tests of the failure path only: an attention
+                                   combiner that finds splits of its kv head still
+                                   missing gives up at once (DEC_ERR_SYNC, its
+                                   output slice not written) instead of polling */
 
 /* Static shape of one decoder layer (identical for every layer of a stack). */
 typedef struct {
@@ -96,7 +100,7 @@ typedef struct {
   int32_t ntype;       /* norm weights: DEC_F32 | DEC_BF16 */
   int32_t kvtype;      /* KV cache: DEC_F32 | DEC_BF16 */
   int32_t attn_chunk;  /* cache positions per attention split; 0 = library default */
-  uint32_t flags;      /* DEC_UNFUSED | DEC_NULL_KERNELS */
+  uint32_t flags;      /* DEC_UNFUSED | DEC_NULL_KERNELS | DEC_TEST_NO_WAIT */
 } dec_layer_desc;
 
 /* A weight matrix: `w` the elements, `scales` the per-block fp16 scales

@@ -83,7 +83,8 @@ int main(void) {
   O(dec_layer_state, v_cache) O(dec_layer_state, pos) O(dec_layer_state, rope) O(dec_layer_state, err)
   O(dec_layer_state, scratch)
   printf("DEC_F32 value %d\nDEC_BF16 value %d\nDEC_Q4 value %d\n", DEC_F32, DEC_BF16, DEC_Q4);
-  printf("DEC_UNFUSED value %u\nDEC_NULL_KERNELS value %u\n", DEC_UNFUSED, DEC_NULL_KERNELS);
+  printf("DEC_UNFUSED value %u\nDEC_NULL_KERNELS value %u\nDEC_TEST_NO_WAIT value %u\n", DEC_UNFUSED,
+         DEC_NULL_KERNELS, DEC_TEST_NO_WAIT);
   printf("DEC_ERR_POS value %u\nDEC_ERR_TOKEN value %u\nDEC_ERR_SYNC value %u\n", DEC_ERR_POS, DEC_ERR_TOKEN,
          DEC_ERR_SYNC);
   printf("DEC_COUNTER_STRIDE value %d\n", DEC_COUNTER_STRIDE);
@@ -109,6 +110,7 @@ def test_struct_layout_matches_a_c_compiler(L, tmp_path):
         if field == "value":
             want = {"DEC_F32": L.DEC_F32, "DEC_BF16": L.DEC_BF16, "DEC_Q4": L.DEC_Q4,
                     "DEC_UNFUSED": L.DEC_UNFUSED, "DEC_NULL_KERNELS": L.DEC_NULL_KERNELS,
+                    "DEC_TEST_NO_WAIT": L.DEC_TEST_NO_WAIT,
                     "DEC_ERR_POS": L.DEC_ERR_POS, "DEC_ERR_TOKEN": L.DEC_ERR_TOKEN, "DEC_ERR_SYNC": L.DEC_ERR_SYNC,
                     "DEC_E_NULL": E_NULL, "DEC_E_SHAPE": E_SHAPE, "DEC_E_DTYPE": E_DTYPE,
                     "DEC_E_ALIGN": E_ALIGN, "DEC_COUNTER_STRIDE": L.DEC_COUNTER_STRIDE}[name]
@@ -118,7 +120,7 @@ def test_struct_layout_matches_a_c_compiler(L, tmp_path):
         else:
             assert getattr(getattr(L, name), field).offset == val, f"{name}.{field}"
         seen += 1
-    assert seen == 50   # 4 sizes, 33 offsets, 13 constants
+    assert seen == 51   # 4 sizes, 33 offsets, 14 constants
 
 
 # ---- host-side checks (every call below is rejected before any launch)

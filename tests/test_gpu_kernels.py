@@ -196,6 +196,54 @@ def test_attn_splitk(gpu, d, kvtype, nq, nkv, max_ctx, positions, chunk):
     assert st.check_err() == 0
 
 
+def test_combiner_give_up_sets_sync_error_and_recovers(gpu):
+    """The attention combine's failure path, forced from the host:
+    DEC_TEST_NO_WAIT makes every combiner but the last arrival of a kv head
+    give up its wait at once. Each launch still completes; its only effects
+    are the DEC_ERR_SYNC bit and output slices left unwritten (every output
+    element is either untouched or the oracle's value, and each kv head group
+    has both); the arrival counters are left zero, and the next normal launch
+    on the same buffers is exact."""
+    d, nq, nkv, max_ctx = 128, 32, 8, 4352      # the 9B-shaped layer: several combiners per kv head
+    cfg = synth.tiny(hidden=256, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, ffn=256, wtype="bf16",
+                     ntype="bf16", kvtype="bf16", ctx=0, steps=max_ctx, seed=9)
+    st = DecodeStack(cfg, n_layers=1, flags=L.DEC_TEST_NO_WAIT)
+    std = 0.02 * np.sqrt(4096)
+    K = synth.rand_cache((9, 1, max_ctx), nkv, max_ctx, d, "bf16", std)
+    V = synth.rand_cache((9, 2, max_ctx), nkv, max_ctx, d, "bf16", std)
+    st.set_prefill(0, K, V)
+    Kv = oracle.ref.cache_values(K.data, "bf16", np.float64)
+    Vv = oracle.ref.cache_values(V.data, "bf16", np.float64)
+    group = (nq // nkv) * d
+    for i, p in enumerate((4095, 4351)):
+        q = synth.rand_f32((9, 3, i), (nq, d), std=std)
+        st.q.copy_(torch.from_numpy(q.reshape(-1)))
+        st.set_pos(p)
+        ref = oracle.attend(q.astype(np.float64), Kv[:, : p + 1], Vv[:, : p + 1], nq // nkv).reshape(-1)
+        st.desc.flags = L.DEC_TEST_NO_WAIT
+        st.err.zero_()
+        _fill_sentinel(st.attn)
+        L.dec_attn_splitk(st.desc, st.state[0])
+        torch.cuda.synchronize()
+        assert st.check_err() == L.DEC_ERR_SYNC, f"pos {p}"
+        assert int(st.counters.abs().sum().item()) == 0, "arrival counters not reset"
+        got = st.attn.cpu().numpy()
+        untouched = got.view(np.uint32) == SENT32
+        for j in range(nkv):
+            sl = slice(j * group, (j + 1) * group)
+            assert untouched[sl].any() and not untouched[sl].all(), f"kv head {j}"
+            w = ~untouched[sl]
+            assert rel_l2(got[sl][w], ref[sl][w]) <= TOL, f"kv head {j}: written slice"
+        # the same buffers, the normal path
+        st.desc.flags = 0
+        st.err.zero_()
+        L.dec_attn_splitk(st.desc, st.state[0])
+        torch.cuda.synchronize()
+        assert st.check_err() == 0
+        assert rel_l2(st.attn.cpu().numpy(), ref) <= TOL, f"pos {p}: after the failure"
+        assert int(st.counters.abs().sum().item()) == 0
+
+
 def test_position_out_of_range_sets_error_and_stores_nothing(gpu):
     cfg = _cfg("bf16", "bf16", 256, 4, 4, 64, max_ctx=8)
     lw = synth.layer_weights(cfg, 0)

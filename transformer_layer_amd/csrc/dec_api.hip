@@ -119,6 +119,7 @@ int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t 
   a.max_ctx = d->max_ctx;
   a.kvtype = d->kvtype == DEC_BF16 ? 1 : 0;
   a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
+  a.no_wait = (d->flags & DEC_TEST_NO_WAIT) ? 1 : 0;
   dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
                  &a.chunk, &a.nsplit, &a.waves);
   return launched(dec::launch_attn(a, s), "attn_splitk");

@@ -255,8 +255,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     bool gave_up = false;
     if (slot >= 0 && prev != unsigned(ns - 1)) {
       unsigned n = 0;
-      while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < unsigned(ns)) {
-        if (++n > kSpinMax) {   // give up: flag it, write nothing, still count as finished
+      // (no_wait, tests of this path: give up without polling)
+      const unsigned spin_max = a.no_wait ? 0u : kSpinMax;
+      while (a.no_wait || __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < unsigned(ns)) {
+        if (++n > spin_max) {   // give up: flag it, write nothing, still count as finished
           atomicOr(a.err, kErrSync);
           gave_up = true;
           break;

@@ -90,6 +90,7 @@ struct AttnArgs {
   uint32_t* err;
   int nq, nkv, d, max_ctx, chunk, nsplit, kvtype;
   int waves;           // waves per workgroup (4 or 8)
+  int no_wait;         // combiners give up at once when splits are missing (failure-path tests)
   int null_kernel;
 };
 

@@ -16,6 +16,7 @@ DEC_F32, DEC_BF16, DEC_Q4 = 0, 1, 2
 DTYPES = {"f32": DEC_F32, "bf16": DEC_BF16, "q4": DEC_Q4}
 DEC_UNFUSED = 0x1
 DEC_NULL_KERNELS = 0x2
+DEC_TEST_NO_WAIT = 0x100
 DEC_ERR_POS = 0x1
 DEC_ERR_TOKEN = 0x2
 DEC_ERR_SYNC = 0x4
