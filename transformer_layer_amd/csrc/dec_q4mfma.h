@@ -32,7 +32,7 @@
 // by about 0.9 µs on the 9B-shaped gated FFN). A tile is 8 row pairs (16
 // rows, one per MFMA column); the waves split a tile's steps. A workgroup
 // takes TT adjacent tiles (one, or two when one per workgroup would not fit
-// on the chip at once). Partial sums meet across the four k-groups with lane swaps
+// on the chip at once, or three for large gated FFNs). Partial sums meet across the four k-groups with lane swaps
 // and across waves in LDS, in a fixed order.
 #pragma once
 
