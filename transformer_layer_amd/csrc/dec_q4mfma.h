@@ -212,10 +212,6 @@ __global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
   const int n = lane & 15;   // MFMA column: row n of the tile
   const int g = lane >> 4;   // k-group: block 4s + g of a step
 
-  // The position (QKV epilogue) is read before any other load. (Read after
-  // the weights were requested, as in the bf16 kernels, the 4-bit QKV kernel
-  // ended 0.35 us later: like the second tile's weights, requests that reach
-  // the memory queues before the input has returned delay it.)
   const int G = a.cols / 32;       // blocks per row
   const int S = (G + 3) / 4;       // steps of four blocks
   const int GP = 4 * S;            // blocks with padding
