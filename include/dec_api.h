@@ -198,7 +198,15 @@ int dec_gated_ffn(const dec_layer_desc* desc, const void* ffn_norm, dec_mat wgat
    above in order (or, with DEC_UNFUSED, the ten per-op kernels of the same
    arithmetic: rmsnorm, weight multiply, QKV projection, RoPE + append,
    attention, output projection + residual, rmsnorm with multiply, gate/up
-   projection, SwiGLU, down projection + residual). */
+   projection, SwiGLU, down projection + residual).
+   With bf16 weights and cache (and at most 32 attention splits) the
+   attention's combine moves into the output projection: the attention
+   kernel stops once its partials are written (attn is left as it was), and
+   each workgroup of the projection, owning one kv head group's columns and
+   a block of rows, combines that group's partials while its weights stream
+   and adds its share of Wo a to x with float atomics. The shares of a row
+   add in no fixed order, so repeated runs agree within float32 rounding,
+   not bit for bit. */
 int dec_layer_step(const dec_layer_desc* desc, const dec_layer_weights* w,
                    const dec_layer_state* st, void* stream);
 

@@ -120,7 +120,12 @@ def test_whole_9b_stack_one_token(gpu):
 
 
 @pytest.mark.parametrize("name", ["C4", "C5"])
-def test_fused_equals_unfused_bitwise_at_full_shape(gpu, name):
+def test_fused_matches_unfused_at_full_shape(gpu, name):
+    """4-bit: the per-op kernels share the fused kernels' summation order, so
+    hidden states and caches agree bit for bit. bf16: the fused output
+    projection adds the kv head groups' shares to x with float atomics in no
+    fixed order, so the two agree within float32 reordering (and a bf16
+    cache value may round the other way)."""
     cfg = synth.CONFIGS[name]
     nl, nsteps = 2, 3
     toks = synth.tokens(cfg)
@@ -146,8 +151,18 @@ def test_fused_equals_unfused_bitwise_at_full_shape(gpu, name):
         del st
         _release()
     (xa, Ka, Va), (xb, Kb, Vb) = outs
-    assert np.array_equal(xa.view(np.uint32), xb.view(np.uint32)), f"{name}: hidden states differ"
-    assert torch.equal(Ka, Kb) and torch.equal(Va, Vb), f"{name}: caches differ"
+    if cfg.wtype == "q4":
+        assert np.array_equal(xa.view(np.uint32), xb.view(np.uint32)), f"{name}: hidden states differ"
+        assert torch.equal(Ka, Kb) and torch.equal(Va, Vb), f"{name}: caches differ"
+        return
+    worst = max(rel_l2(xa[s, l], xb[s, l]) for s in range(nsteps) for l in range(1, nl + 1))
+    assert worst <= 1e-5, f"{name}: fused vs per-op relative L2 {worst:.3e}"
+    # caches: prefill and unwritten slots identical, decoded slots within one bf16 step
+    assert torch.equal(Ka[:, :, : cfg.ctx], Kb[:, :, : cfg.ctx]) and torch.equal(Va[:, :, : cfg.ctx], Vb[:, :, : cfg.ctx])
+    for A, B in ((Ka, Kb), (Va, Vb)):
+        a = A[:, :, cfg.ctx: cfg.ctx + nsteps].view(torch.bfloat16).float()
+        b = B[:, :, cfg.ctx: cfg.ctx + nsteps].view(torch.bfloat16).float()
+        assert bool(((a - b).abs() <= a.abs() * 2.0 ** -7).all()), f"{name}: decoded cache slots differ"
 
 
 GREEDY = sorted(os.path.basename(p)[len("greedy_"):-len(".json")] for p in glob.glob(os.path.join(GOLD, "greedy_*.json")))

@@ -102,7 +102,7 @@ int qkv_launch(const dec_layer_desc* d, const dec_layer_weights* w, const dec_la
   return launched(gemv(d->wtype, dec::kEpiQkv, a, s), "rmsnorm_gemv_qkv_rope");
 }
 
-int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t s) {
+int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t s, bool partials_only = false) {
   dec::AttnArgs a;
   memset(&a, 0, sizeof a);
   a.q = st->q;
@@ -120,9 +120,38 @@ int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t 
   a.kvtype = d->kvtype == DEC_BF16 ? 1 : 0;
   a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
   a.no_wait = (d->flags & DEC_TEST_NO_WAIT) ? 1 : 0;
+  a.partials_only = partials_only ? 1 : 0;
   dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
                  &a.chunk, &a.nsplit, &a.waves);
   return launched(dec::launch_attn(a, s), "attn_splitk");
+}
+
+// The fused layer combines attention inside the output projection for bf16
+// weights and cache when the split count allows it.
+bool attn_o_path(const dec_layer_desc* d) {
+  if (d->wtype != DEC_BF16 || d->kvtype != DEC_BF16 || (d->flags & DEC_TEST_NO_WAIT)) return false;
+  int chunk, ns, nw;
+  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, 1, d->max_ctx, d->attn_chunk, &chunk, &ns, &nw);
+  return dec::attn_o_supported(d->n_q_heads, d->n_kv_heads, d->head_dim, ns);
+}
+
+int attn_o_launch(const dec_layer_desc* d, dec_mat wo, const dec_layer_state* st, hipStream_t s) {
+  dec::AttnOArgs a;
+  memset(&a, 0, sizeof a);
+  a.part = st->part;
+  a.W = wo.w;
+  a.x = st->x;
+  a.pos = st->pos;
+  a.nq = d->n_q_heads;
+  a.nkv = d->n_kv_heads;
+  a.d = d->head_dim;
+  a.rows = d->hidden;
+  a.cols = d->n_q_heads * d->head_dim;
+  a.max_ctx = d->max_ctx;
+  a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
+  int nw;
+  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, 1, d->max_ctx, d->attn_chunk, &a.chunk, &a.nsplit, &nw);
+  return launched(dec::launch_attn_o(a, s), "attn_o");
 }
 
 int residual_launch(const dec_layer_desc* d, dec_mat w, int rows, int cols, const float* in,
@@ -253,8 +282,13 @@ int dec_layer_step(const dec_layer_desc* d, const dec_layer_weights* w, const de
   const int H = d->hidden, F = d->ffn, qd = d->n_q_heads * d->head_dim;
   if (!unfused) {
     if ((rc = qkv_launch(d, w, st, s))) return rc;
-    if ((rc = attn_launch(d, st, s))) return rc;
-    if ((rc = residual_launch(d, w->wo, H, qd, st->attn, st->x, s))) return rc;
+    if (attn_o_path(d)) {
+      if ((rc = attn_launch(d, st, s, true))) return rc;
+      if ((rc = attn_o_launch(d, w->wo, st, s))) return rc;
+    } else {
+      if ((rc = attn_launch(d, st, s))) return rc;
+      if ((rc = residual_launch(d, w->wo, H, qd, st->attn, st->x, s))) return rc;
+    }
     if ((rc = ffn_launch(d, w->ffn_norm, w->wgate, w->wup, st->x, st->h, s))) return rc;
     return residual_launch(d, w->wdown, H, F, st->h, st->x, s);
   }

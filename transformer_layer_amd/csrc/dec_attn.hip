@@ -238,6 +238,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   for (int i2 = threadIdx.x; i2 < G * D / 2; i2 += kBlock) store_pair_agent(po + 2 * i2, osum(2 * i2), osum(2 * i2 + 1));
   if (threadIdx.x < G) store_pair_agent(pml + threadIdx.x * 2, stat[threadIdx.x][0], stat[threadIdx.x][1]);
 
+  if (a.partials_only) return;   // the output projection combines them
+
   // ---- arrival. The last ncomb splits of this kv head to arrive each
   // combine a slice of its outputs: the earlier ones wait (bounded) until
   // every split has arrived. Word 0 of the head's counter line counts

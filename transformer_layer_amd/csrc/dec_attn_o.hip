@@ -1,0 +1,177 @@
+// Attention combine fused into the output projection (bf16 weights and
+// cache): x += Wo a, where a is combined here from the split-K attention's
+// partials instead of by the attention kernel's last workgroups.
+//
+// Workgroup (j, rb) owns kv head j's query-head group (C = g d columns of Wo)
+// and a block of R output rows. It requests, in this order, the (max, sum)
+// partials of head j's splits, their unnormalized outputs for its columns,
+// and its Wo block (R rows x C columns), so that waiting for the partials
+// never waits for the weights (loads complete in order). It then forms the
+// head group's attention output
+//   a_c = sum_s w_s o_s,c,  w_s = exp2(m_s - M) / sum_s' exp2(m_s' - M) l_s'
+// (M the largest split max, scores in log2 units) in LDS, takes the dot
+// products of its rows with it, and adds them to x with float atomics: the
+// n_kv head groups of a row add in no fixed order. The combine's latency is
+// spent while the weights stream, instead of as a chain of round trips at
+// the end of the attention kernel.
+#include "dec_device.h"
+#include "dec_internal.h"
+
+namespace dec {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int C, int NL>
+__global__ __launch_bounds__(512) void attn_o_kernel(AttnOArgs a) {
+  constexpr int NW = 8, NT = 512;
+  constexpr int LPR = C / 8;             // lanes per Wo row (bf16 granules of 8 columns)
+  constexpr int RPW = 64 / LPR;          // rows per wave load
+  constexpr int R = NL * RPW * NW;       // rows per workgroup
+  constexpr int CG = C / 4;              // float4 column groups of the head group
+  constexpr int SL = NT / CG;            // threads per column group (each a subset of the splits)
+  constexpr int NO = kAttnOSplits / SL;  // partial-output loads per thread
+  static_assert(LPR >= 8 && LPR <= 64 && SL >= 1 && kAttnOSplits % SL == 0, "shape");
+
+  if (a.null_kernel) return;
+  const int j = blockIdx.x % a.nkv;
+  const int rb = blockIdx.x / a.nkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int G = C / a.d;
+  const int last = a.nsplit - 1;
+
+  // (max, sum) of split s for head h: thread t takes (h, s) = (t / 32, t % 32)
+  // of its head group (threads past G*32 repeat a valid pair, unused)
+  const float* pml = a.part + size_t(a.nkv) * a.nsplit * C + size_t(j) * a.nsplit * G * 2;
+  const int ml_t = tid % (G * kAttnOSplits);
+  const int ml_h = ml_t / kAttnOSplits, ml_s = ml_t % kAttnOSplits;
+  const float2 ml = *reinterpret_cast<const float2*>(pml + (size_t(min(ml_s, last)) * G + ml_h) * 2);
+
+  // unnormalized outputs: thread t takes column group t % CG and splits
+  // t / CG, + SL, ... (clamped to the splits the buffer holds)
+  const int cg = tid % CG, sl = tid / CG;
+  const float* po = a.part + size_t(j) * a.nsplit * C;
+  float4 ov[NO];
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const int s = min(sl + k * SL, last);
+    ov[k] = *reinterpret_cast<const float4*>(po + size_t(s) * C + cg * 4);
+  }
+
+  // this workgroup's Wo rows: lane (sub, li) of wave wv takes rows
+  // r0 + wv*NL*RPW + u*RPW + sub, columns j*C + li*8 .. +7
+  const int sub = lane / LPR, li = lane % LPR;
+  const int r0 = rb * R + wv * NL * RPW + sub;
+  const uint8_t* W = reinterpret_cast<const uint8_t*>(a.W);
+  u32x4 wq[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int r = min(r0 + u * RPW, a.rows - 1);
+    wq[u] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(W + (size_t(r) * a.cols + size_t(j) * C + li * 8) * 2));
+  }
+
+  // the position decides which splits hold cache rows
+  const int pos = *a.pos;
+  if (pos < 0 || pos >= a.max_ctx) return;   // the attention kernel flagged it and wrote nothing
+  const int ns = (pos + a.chunk) / a.chunk;  // splits over positions 0..pos
+
+  __shared__ float wts[8][kAttnOSplits];      // per head and split: exp2(m - M) / den
+  __shared__ float4 red[NT];
+  __shared__ float av[C];
+
+  // weights: groups of 32 lanes hold one head's splits
+  {
+    const bool ok = ml_s < ns;
+    const float m = ok ? ml.x : -INFINITY;
+    const float M = group_max<32>(m);
+    const float w = ok ? exp2f(ml.x - M) : 0.0f;
+    const float den = group_sum<32>(ok ? w * ml.y : 0.0f);  // >= 1: the split holding M adds l >= 1
+    if (tid < G * kAttnOSplits) wts[ml_h][ml_s] = w / den;
+  }
+  __syncthreads();
+  {
+    const int h = (cg * 4) / a.d;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < NO; ++k) {
+      // splits past ns hold whatever an earlier token (or nothing) left
+      // there: skipped, so that no stale value reaches the sum as 0 * inf
+      const bool live = sl + k * SL < ns;
+      const float w = live ? wts[h][sl + k * SL] : 0.0f;
+      const float4 o = live ? ov[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+      acc.x = fmaf(w, o.x, acc.x); acc.y = fmaf(w, o.y, acc.y);
+      acc.z = fmaf(w, o.z, acc.z); acc.w = fmaf(w, o.w, acc.w);
+    }
+    red[tid] = acc;
+  }
+  __syncthreads();
+  if (tid < CG) {
+    float4 s4 = red[tid];
+#pragma unroll
+    for (int k = 1; k < SL; ++k) {
+      const float4 v = red[k * CG + tid];
+      s4.x += v.x; s4.y += v.y; s4.z += v.z; s4.w += v.w;
+    }
+    av[tid * 4] = s4.x; av[tid * 4 + 1] = s4.y; av[tid * 4 + 2] = s4.z; av[tid * 4 + 3] = s4.w;
+  }
+  __syncthreads();
+
+  // dot products of this lane's rows with its eight columns, summed over the
+  // row's lanes, added to x
+  float u8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) u8[e] = av[li * 8 + e];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const u32x4 w = wq[u];
+    float acc = 0.0f;
+    acc = fmaf(bf_lo(w.x), u8[0], acc); acc = fmaf(bf_hi(w.x), u8[1], acc);
+    acc = fmaf(bf_lo(w.y), u8[2], acc); acc = fmaf(bf_hi(w.y), u8[3], acc);
+    acc = fmaf(bf_lo(w.z), u8[4], acc); acc = fmaf(bf_hi(w.z), u8[5], acc);
+    acc = fmaf(bf_lo(w.w), u8[6], acc); acc = fmaf(bf_hi(w.w), u8[7], acc);
+    acc = group_sum<LPR>(acc);
+    const int r = r0 + u * RPW;
+    if (li == 0 && r < a.rows) atomicAdd(a.x + r, acc);
+  }
+}
+
+// rows per lane: the most (16, 8 or 4) that still gives every CU a workgroup
+static int attn_o_nl(int rows, int nkv, int C) {
+  const int rpw = 64 / (C / 8);
+  for (int nl : {16, 8, 4}) {
+    const int per_wg = nl * rpw * 8;
+    if (nkv * ((rows + per_wg - 1) / per_wg) >= 256) return nl;
+  }
+  return 4;
+}
+
+bool attn_o_supported(int n_q, int n_kv, int head_dim, int nsplit) {
+  const int C = (n_q / n_kv) * head_dim;
+  return nsplit <= kAttnOSplits && (C == 128 || C == 256 || C == 512) && n_q / n_kv <= 8;
+}
+
+template <int C>
+static hipError_t go_attn_o(const AttnOArgs& a, hipStream_t s) {
+  const int nl = attn_o_nl(a.rows, a.nkv, C);
+  const int rpw = 64 / (C / 8);
+  const int per_wg = nl * rpw * 8;
+  const dim3 grid(a.nkv * ((a.rows + per_wg - 1) / per_wg)), block(512);
+  if (nl == 16) hipLaunchKernelGGL((attn_o_kernel<C, 16>), grid, block, 0, s, a);
+  else if (nl == 8) hipLaunchKernelGGL((attn_o_kernel<C, 8>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attn_o_kernel<C, 4>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_o(const AttnOArgs& a, hipStream_t s) {
+  if (a.nsplit > kAttnOSplits) return hipErrorInvalidValue;
+  switch ((a.nq / a.nkv) * a.d) {
+    case 128: return go_attn_o<128>(a, s);
+    case 256: return go_attn_o<256>(a, s);
+    case 512: return go_attn_o<512>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dec

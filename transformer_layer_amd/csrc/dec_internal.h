@@ -91,6 +91,7 @@ struct AttnArgs {
   int nq, nkv, d, max_ctx, chunk, nsplit, kvtype;
   int waves;           // waves per workgroup (4 or 8)
   int no_wait;         // combiners give up at once when splits are missing (failure-path tests)
+  int partials_only;   // write the splits' partials and stop (the output projection combines them)
   int null_kernel;
 };
 
@@ -98,6 +99,20 @@ struct AttnArgs {
 void attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit,
                int* waves);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+// Attention combine fused into the output projection (bf16): x += Wo a, a
+// combined from the partials of at most kAttnOSplits splits per kv head.
+constexpr int kAttnOSplits = 32;
+struct AttnOArgs {
+  const float* part;   // the attention kernel's partials (layout of AttnArgs::part)
+  const void* W;       // Wo, bf16 [rows][cols]
+  float* x;            // [rows], updated with float atomics
+  const int32_t* pos;
+  int nq, nkv, d, rows, cols, nsplit, chunk, max_ctx;
+  int null_kernel;
+};
+bool attn_o_supported(int n_q, int n_kv, int head_dim, int nsplit);
+hipError_t launch_attn_o(const AttnOArgs& a, hipStream_t s);
 
 // small per-op and per-token kernels
 // RMSNorm (optionally times its weight) with the fused kernels' summation
