@@ -138,7 +138,9 @@ def test_bf16_attention_combined_in_output_projection(gpu, hidden, nq, nkv, d, f
     b = _run_gpu_eager(st_u, toks, 0)
     diff = max(rel_l2(a[s, l], b[s, l]) for s in range(len(toks)) for l in range(1, cfg.n_layers + 1))
     print(f"fused vs oracle {worst:.2e}, fused vs per-op {diff:.2e}")
-    assert diff <= 1e-4, diff
+    # float32 reordering of x, plus now and then a bf16 cache value that
+    # rounds the other way (about 1e-6 each here)
+    assert diff <= 2e-5, diff
 
     st_g, _ = _build(cfg)
     st_g.set_token_list(toks)
