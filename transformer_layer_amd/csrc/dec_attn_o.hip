@@ -21,7 +21,7 @@ namespace dec {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int C, int NL>
+template <int C, int NL, int NO>
 __global__ __launch_bounds__(512) void attn_o_kernel(AttnOArgs a) {
   constexpr int NW = 8, NT = 512;
   constexpr int LPR = C / 8;             // lanes per Wo row (bf16 granules of 8 columns)
@@ -29,8 +29,8 @@ __global__ __launch_bounds__(512) void attn_o_kernel(AttnOArgs a) {
   constexpr int R = NL * RPW * NW;       // rows per workgroup
   constexpr int CG = C / 4;              // float4 column groups of the head group
   constexpr int SL = NT / CG;            // threads per column group (each a subset of the splits)
-  constexpr int NO = kAttnOSplits / SL;  // partial-output loads per thread
-  static_assert(LPR >= 8 && LPR <= 64 && SL >= 1 && kAttnOSplits % SL == 0, "shape");
+  // NO partial-output loads per thread: NO * SL >= the plan's split count
+  static_assert(LPR >= 8 && LPR <= 64 && SL >= 1 && NO >= 1 && NO * SL <= kAttnOSplits, "shape");
 
   if (a.null_kernel) return;
   const int j = blockIdx.x % a.nkv;
@@ -158,16 +158,40 @@ bool attn_o_supported(int n_q, int n_kv, int head_dim, int nsplit) {
   return nsplit <= kAttnOSplits && (C == 128 || C == 256 || C == 512) && n_q / n_kv <= 8;
 }
 
+template <int C, int NL, int NO>
+static void go_attn_o_no(const AttnOArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((attn_o_kernel<C, NL, NO>), grid, dim3(512), 0, s, a);
+}
+
+// partial-output loads per thread: the fewest that cover the plan's splits
+// (splits past the last would only re-read it)
+template <int C, int NL>
+static hipError_t go_attn_o_nl(const AttnOArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int SL = 512 / (C / 4);
+  const int no = (a.nsplit + SL - 1) / SL;
+  switch (no) {
+    case 1: go_attn_o_no<C, NL, 1>(a, grid, s); break;
+    case 2: go_attn_o_no<C, NL, 2>(a, grid, s); break;
+    case 3: if constexpr (3 * SL <= kAttnOSplits) { go_attn_o_no<C, NL, 3>(a, grid, s); break; } return hipErrorInvalidValue;
+    case 4: if constexpr (4 * SL <= kAttnOSplits) { go_attn_o_no<C, NL, 4>(a, grid, s); break; } return hipErrorInvalidValue;
+    case 5: if constexpr (5 * SL <= kAttnOSplits) { go_attn_o_no<C, NL, 5>(a, grid, s); break; } return hipErrorInvalidValue;
+    case 6: if constexpr (6 * SL <= kAttnOSplits) { go_attn_o_no<C, NL, 6>(a, grid, s); break; } return hipErrorInvalidValue;
+    case 7: if constexpr (7 * SL <= kAttnOSplits) { go_attn_o_no<C, NL, 7>(a, grid, s); break; } return hipErrorInvalidValue;
+    case 8: if constexpr (8 * SL <= kAttnOSplits) { go_attn_o_no<C, NL, 8>(a, grid, s); break; } return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int C>
 static hipError_t go_attn_o(const AttnOArgs& a, hipStream_t s) {
   const int nl = attn_o_nl(a.rows, a.nkv, C);
   const int rpw = 64 / (C / 8);
   const int per_wg = nl * rpw * 8;
-  const dim3 grid(a.nkv * ((a.rows + per_wg - 1) / per_wg)), block(512);
-  if (nl == 16) hipLaunchKernelGGL((attn_o_kernel<C, 16>), grid, block, 0, s, a);
-  else if (nl == 8) hipLaunchKernelGGL((attn_o_kernel<C, 8>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((attn_o_kernel<C, 4>), grid, block, 0, s, a);
-  return hipGetLastError();
+  const dim3 grid(a.nkv * ((a.rows + per_wg - 1) / per_wg));
+  if (nl == 16) return go_attn_o_nl<C, 16>(a, grid, s);
+  if (nl == 8) return go_attn_o_nl<C, 8>(a, grid, s);
+  return go_attn_o_nl<C, 4>(a, grid, s);
 }
 
 hipError_t launch_attn_o(const AttnOArgs& a, hipStream_t s) {
