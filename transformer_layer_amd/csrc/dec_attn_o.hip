@@ -119,7 +119,9 @@ __global__ __launch_bounds__(512) void attn_o_kernel(AttnOArgs a) {
   __syncthreads();
 
   // dot products of this lane's rows with its eight columns, summed over the
-  // row's lanes, added to x
+  // row's lanes, staged in LDS (the workgroup's rows are contiguous) and
+  // added to x by consecutive threads, so that the atomics coalesce
+  __shared__ float rsum[R];
   float u8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) u8[e] = av[li * 8 + e];
@@ -132,8 +134,12 @@ __global__ __launch_bounds__(512) void attn_o_kernel(AttnOArgs a) {
     acc = fmaf(bf_lo(w.z), u8[4], acc); acc = fmaf(bf_hi(w.z), u8[5], acc);
     acc = fmaf(bf_lo(w.w), u8[6], acc); acc = fmaf(bf_hi(w.w), u8[7], acc);
     acc = group_sum<LPR>(acc);
-    const int r = r0 + u * RPW;
-    if (li == 0 && r < a.rows) atomicAdd(a.x + r, acc);
+    if (li == 0) rsum[wv * NL * RPW + u * RPW + sub] = acc;
+  }
+  __syncthreads();
+  for (int i = tid; i < R; i += NT) {
+    const int r = rb * R + i;
+    if (r < a.rows) atomicAdd(a.x + r, rsum[i]);
   }
 }
 
