@@ -109,9 +109,11 @@ def test_graph_replay_equals_eager(gpu):
     assert torch.equal(st_g.K, st_e.K)
 
 
-# (hidden, n_q, n_kv, d, ffn): 256, 128 and 512 output-projection columns per
-# kv head group; hidden not a multiple of any row block
-ATTN_O = [(1000, 8, 2, 64, 344), (520, 4, 4, 128, 200), (1032, 16, 2, 64, 264)]
+# (hidden, n_q, n_kv, d, ffn): output-projection column blocks of 256, 128,
+# 512 and 64 columns (one per kv head group), and of one 128-wide head of a
+# group of four; hidden not a multiple of any row block
+ATTN_O = [(1000, 8, 2, 64, 344), (520, 4, 4, 128, 200), (1032, 16, 2, 64, 264), (1000, 4, 4, 64, 200),
+          (1040, 8, 2, 128, 344)]
 
 
 @pytest.mark.parametrize("hidden,nq,nkv,d,ffn", ATTN_O)
