@@ -129,9 +129,12 @@ typedef struct {
 typedef struct {
   float* x;            /* [H] residual stream, read and updated in place */
   float* q;            /* [n_q d] rotated queries (written by the QKV kernel) */
-  float* attn;         /* [n_q d] attention output, heads in order */
+  float* attn;         /* [n_q d] attention output, heads in order (the bf16
+                          layer step combines inside the output projection
+                          and leaves it untouched) */
   float* h;            /* [F] SwiGLU output, input of the down projection */
-  float* part;         /* [dec_attn_part_floats(desc)] split partials, 16-byte aligned */
+  float* part;         /* [dec_attn_part_floats(desc)] split partials, 16-byte
+                          aligned; any contents between calls */
   uint32_t* counters;  /* [n_kv * DEC_COUNTER_STRIDE] arrival counters; zero
                           before first use, and the attention kernel leaves
                           them zero */
