@@ -27,7 +27,7 @@ __global__ __launch_bounds__(512) void attn_o_kernel(AttnOArgs a) {
   constexpr int LPR = C / 8;             // lanes per Wo row (bf16 granules of 8 columns)
   constexpr int RPW = 64 / LPR;          // rows per wave load
   constexpr int R = NL * RPW * NW;       // rows per workgroup
-  constexpr int CG = C / 4;              // float4 column groups of the head group
+  constexpr int CG = C / 4;              // float4 column groups of the block
   constexpr int SL = NT / CG;            // threads per column group (each a subset of the splits)
   // NO partial-output loads per thread: NO * SL >= the plan's split count
   static_assert(LPR >= 8 && LPR <= 64 && SL >= 1 && NO >= 1 && NO * SL <= kAttnOSplits, "shape");
