@@ -32,8 +32,8 @@ PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 # sources whose code the gated-FFN kernel is built from
 FFN_SOURCES = ["transformer_layer_amd/csrc/dec_gemv.h", "transformer_layer_amd/csrc/dec_device.h",
-               "transformer_layer_amd/csrc/dec_internal.h", "transformer_layer_amd/csrc/dec_gemv_bf16.hip",
-               "transformer_layer_amd/csrc/dec_gemv_q4.hip", "transformer_layer_amd/csrc/dec_gemv_f32.hip"]
+               "transformer_layer_amd/csrc/dec_internal.h", "transformer_layer_amd/csrc/dec_gemv_dense.hip",
+               "transformer_layer_amd/csrc/dec_gemv_q4.hip", "transformer_layer_amd/csrc/dec_q4mfma.h"]
 
 
 def log(msg: str) -> None:

@@ -14,8 +14,11 @@
  * multiply in the preamble of the following projection, RoPE folded into the
  * QKV projection's epilogue, and gate, up and SwiGLU as one gated-FFN kernel
  * whose wide intermediate never reaches memory. A fused layer is five
- * kernels: dec_rmsnorm_gemv_qkv_rope, dec_attn_splitk, dec_gemv_residual
- * (output projection), dec_gated_ffn, dec_gemv_residual (down projection).
+ * kernels: dec_rmsnorm_gemv_qkv_rope, the attention (dec_attn_splitk, or
+ * dec_attn_partials with bf16 weights and cache), the output projection with
+ * the residual add (dec_gemv_residual, or dec_attn_o_residual, which also
+ * combines the attention's partials), dec_gated_ffn, dec_gemv_residual (down
+ * projection); dec_layer_step runs them in order.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -54,7 +57,7 @@
 extern "C" {
 #endif
 
-#define DEC_ABI_VERSION 2
+#define DEC_ABI_VERSION 3
 
 enum dec_dtype { DEC_F32 = 0, DEC_BF16 = 1, DEC_Q4 = 2 };
 
@@ -79,13 +82,34 @@ enum dec_status {
 #define DEC_ERR_SYNC 0x4u  /* an attention combiner stopped waiting for the other
                               splits of its kv head; that output slice is not written */
 
-/* dec_layer_desc.flags */
-#define DEC_UNFUSED 0x1u       /* dec_layer_step runs the ten per-op kernels */
-#define DEC_NULL_KERNELS 0x2u  /* same launches, every kernel body returns at once */
-#define DEC_TEST_NO_WAIT 0x100u /* tests of the failure path only: an attention
-                                   combiner that finds splits of its kv head still
-                                   missing gives up at once (DEC_ERR_SYNC, its
-                                   output slice not written) instead of polling */
+/* dec_layer_desc.flags.
+   Fusion controls, global and per fused operation ("backend-specific kernel
+   fusion", sections "A practical engineering example" and "What you can do
+   this week": every fused path can be switched off on its own and all of
+   them at once, and the unfused path computes the same arithmetic): */
+#define DEC_UNFUSED 0x1u        /* all three below: dec_layer_step runs the ten per-op kernels */
+#define DEC_NULL_KERNELS 0x2u   /* same launches, every kernel body returns at once */
+#define DEC_NO_FUSE_QKV 0x4u    /* the first kernel as rmsnorm, weight multiply, QKV projection,
+                                   RoPE + append (four kernels) */
+#define DEC_NO_FUSE_FFN 0x8u    /* the gated FFN as rmsnorm with multiply, gate/up projection,
+                                   SwiGLU (three kernels) */
+#define DEC_NO_FUSE_ATTN_O 0x10u /* the attention combines its own splits and the output
+                                    projection is a plain dec_gemv_residual */
+#define DEC_DETERMINISTIC 0x20u /* no float atomics on the path, so repeated runs give the
+                                   same bits (takes the DEC_NO_FUSE_ATTN_O path) */
+/* Tests only. DEC_TEST_NO_WAIT exercises a failure path: an attention
+   combiner that finds splits of its kv head still missing gives up at once
+   (DEC_ERR_SYNC, its output slice not written) instead of polling. The
+   three faults below make the fused kernels' numbers wrong on purpose
+   (every kernel still completes and stores in bounds), so a parity test can
+   show that it fails on a wrong kernel ("Kernel fusion and block bridging",
+   section "What it keeps": the gates are run against violations). */
+#define DEC_TEST_NO_WAIT 0x100u
+#define DEC_TEST_SKIP_ROPE 0x200u   /* the fused QKV kernel leaves q and k unrotated */
+#define DEC_TEST_APPEND_NEXT 0x400u /* the fused QKV kernel stores k, v at position p + 1
+                                       (at p when p + 1 is past the cache) */
+#define DEC_TEST_DROP_SPLIT 0x800u  /* attention combines leave out the last split
+                                       (when there are two or more) */
 
 /* Static shape of one decoder layer (identical for every layer of a stack). */
 typedef struct {
@@ -100,7 +124,7 @@ typedef struct {
   int32_t ntype;       /* norm weights: DEC_F32 | DEC_BF16 */
   int32_t kvtype;      /* KV cache: DEC_F32 | DEC_BF16 */
   int32_t attn_chunk;  /* cache positions per attention split; 0 = library default */
-  uint32_t flags;      /* DEC_UNFUSED | DEC_NULL_KERNELS | DEC_TEST_NO_WAIT */
+  uint32_t flags;      /* DEC_* flags above */
 } dec_layer_desc;
 
 /* A weight matrix: `w` the elements, `scales` the per-block fp16 scales
@@ -143,8 +167,9 @@ typedef struct {
   const int32_t* pos;  /* position p of the token being decoded */
   const float* rope;   /* [max_ctx][d/2][2] (cos, sin) from dec_rope_table */
   uint32_t* err;       /* device error word (bits are OR-ed in) */
-  float* scratch;      /* [dec_scratch_floats(desc)]; used by DEC_UNFUSED only,
-                          may be NULL otherwise */
+  float* scratch;      /* [dec_scratch_floats(desc)]; used by DEC_UNFUSED,
+                          DEC_NO_FUSE_QKV and DEC_NO_FUSE_FFN only, may be
+                          NULL otherwise */
 } dec_layer_state;
 
 /* ---- sizes of caller-provided buffers ---------------------------------- */
@@ -173,13 +198,42 @@ int dec_rmsnorm_gemv_qkv_rope(const dec_layer_desc* desc, const dec_layer_weight
 /* Decode attention of the token's queries over cache positions 0..p,
    split along the positions ("split-K"): each workgroup reduces one chunk of
    one kv head for all of its query heads into (max, sum, unnormalized
-   output) partials, and the last workgroup of a kv head to arrive combines
-   them with a log-sum-exp rescale. Passage: "RDNA4 Decode Kernel Fusion...",
+   output) partials, and the last workgroups of a kv head to arrive (up to
+   eight, each a slice of the head group's outputs) combine them with a
+   log-sum-exp rescale. Passage: "RDNA4 Decode Kernel Fusion...",
    sections "Decode is where the bubble has nowhere to go" (attention against
    the KV cache) and "Where fusion stops" (attention stays its own kernel).
    Query head h uses kv head h / (n_q/n_kv); scores are scaled by 1/sqrt(d).
-   Reads: q, caches, pos. Writes: attn, part, counters (left zero), err. */
+   The last arrivals of a kv head combine in a fixed order (each output
+   element sums its splits in split order), so repeated runs give the same
+   bits. Reads: q, caches, pos. Writes: attn, part, counters (left zero),
+   err. */
 int dec_attn_splitk(const dec_layer_desc* desc, const dec_layer_state* st, void* stream);
+
+/* The attention's first half on its own: the same split-K reduction as
+   dec_attn_splitk, stopping once every split's partials are in `part`
+   (o [n_kv][splits][g][d] unnormalized, then (m, l) [n_kv][splits][g][2]
+   with m in log2 units); nothing is combined and attn, counters are left
+   as they were. Passage: "RDNA4 Decode Kernel Fusion...", section "Where
+   fusion stops" (attention is the one step that stays its own kernel; what
+   follows it is the output projection). Reads: q, caches, pos. Writes:
+   part, err. */
+int dec_attn_partials(const dec_layer_desc* desc, const dec_layer_state* st, void* stream);
+
+/* The attention's combine fused into the output projection with its
+   residual add: x += Wo a, where a is formed inside this kernel from the
+   partials dec_attn_partials left in st->part (a log-sum-exp rescale per
+   head and split), so the attention output never reaches memory. Passage:
+   "RDNA4 Decode Kernel Fusion...", sections "Where fusion stops" (the
+   output projection after attention) and "Fusion removes the barrier by
+   removing the write" (an intermediate that is not written needs no
+   barrier). Each workgroup owns one column block of Wo (one query head,
+   or a kv head's whole group of 64-wide heads) and a block of rows, and
+   adds its rows' share to x with float atomics: repeated runs agree within
+   float32 rounding, not bit for bit. Requires bf16 weights and cache and at
+   most 32 attention splits for desc (DEC_E_UNSUPPORTED otherwise, and under
+   DEC_DETERMINISTIC). Reads: part, wo, pos. Writes: x. */
+int dec_attn_o_residual(const dec_layer_desc* desc, dec_mat wo, const dec_layer_state* st, void* stream);
 
 /* x += W in: a projection fused with the residual add ("RDNA4 Decode Kernel
    Fusion...", section "Decode is where the bubble has nowhere to go": output
@@ -197,19 +251,29 @@ int dec_gemv_residual(const dec_layer_desc* desc, dec_mat w, int32_t rows, int32
 int dec_gated_ffn(const dec_layer_desc* desc, const void* ffn_norm, dec_mat wgate, dec_mat wup,
                   const float* x, float* h, void* stream);
 
-/* One whole decoder layer for the token at position *pos: the five kernels
-   above in order (or, with DEC_UNFUSED, the ten per-op kernels of the same
-   arithmetic: rmsnorm, weight multiply, QKV projection, RoPE + append,
-   attention, output projection + residual, rmsnorm with multiply, gate/up
-   projection, SwiGLU, down projection + residual).
-   With bf16 weights and cache (and at most 32 attention splits) the
-   attention's combine moves into the output projection: the attention
-   kernel stops once its partials are written (attn is left as it was), and
-   each workgroup of the projection, owning one kv head group's columns and
-   a block of rows, combines that group's partials while its weights stream
-   and adds its share of Wo a to x with float atomics. The shares of a row
-   add in no fixed order, so repeated runs agree within float32 rounding,
-   not bit for bit. */
+/* One whole decoder layer for the token at position *pos, in the order
+   "RDNA4 Decode Kernel Fusion: Pipeline Barriers, Not Launches, Are the Win"
+   gives in section "Decode is where the bubble has nowhere to go" (norm,
+   QKV projection, RoPE, attention, output projection, norm, gate/up,
+   SwiGLU, down), with the fusions of its section "Fusion removes the
+   barrier by removing the write" and of its opening questions (norm in the
+   projection's preamble, RoPE in the QKV epilogue, gate, up and SwiGLU in
+   one kernel). Pre-norm residual structure: x += O(attention(norm(x))),
+   then x += down(ffn(norm(x))).
+   Five kernels: dec_rmsnorm_gemv_qkv_rope, the attention, the output
+   projection with the residual add, dec_gated_ffn, dec_gemv_residual
+   (down). With bf16 weights and cache (and at most 32 attention splits)
+   the attention is dec_attn_partials and the output projection
+   dec_attn_o_residual (the combine inside the projection, float atomics
+   into x); otherwise dec_attn_splitk and dec_gemv_residual.
+   Flags: DEC_NO_FUSE_QKV, DEC_NO_FUSE_FFN and DEC_NO_FUSE_ATTN_O switch off
+   one fused operation each (DEC_DETERMINISTIC takes the atomics-free
+   path); DEC_UNFUSED switches off all three: ten per-op kernels (rmsnorm,
+   weight multiply, QKV projection, RoPE + append, attention, output
+   projection + residual, rmsnorm with multiply, gate/up projection,
+   SwiGLU, down projection + residual), whose f32 and 4-bit results equal
+   the fused ones bit for bit. st->scratch is needed when DEC_UNFUSED,
+   DEC_NO_FUSE_QKV or DEC_NO_FUSE_FFN is set. */
 int dec_layer_step(const dec_layer_desc* desc, const dec_layer_weights* w,
                    const dec_layer_state* st, void* stream);
 

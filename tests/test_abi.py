@@ -18,7 +18,7 @@ import synth
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dec_api.h")
 
-DEC_OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN = 0, -1, -2, -3, -4
+DEC_OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_UNSUPPORTED = 0, -1, -2, -3, -4, -6
 
 
 @pytest.fixture(scope="module")
@@ -85,6 +85,11 @@ int main(void) {
   printf("DEC_F32 value %d\nDEC_BF16 value %d\nDEC_Q4 value %d\n", DEC_F32, DEC_BF16, DEC_Q4);
   printf("DEC_UNFUSED value %u\nDEC_NULL_KERNELS value %u\nDEC_TEST_NO_WAIT value %u\n", DEC_UNFUSED,
          DEC_NULL_KERNELS, DEC_TEST_NO_WAIT);
+  printf("DEC_NO_FUSE_QKV value %u\nDEC_NO_FUSE_FFN value %u\nDEC_NO_FUSE_ATTN_O value %u\n", DEC_NO_FUSE_QKV,
+         DEC_NO_FUSE_FFN, DEC_NO_FUSE_ATTN_O);
+  printf("DEC_DETERMINISTIC value %u\nDEC_TEST_SKIP_ROPE value %u\nDEC_TEST_APPEND_NEXT value %u\n",
+         DEC_DETERMINISTIC, DEC_TEST_SKIP_ROPE, DEC_TEST_APPEND_NEXT);
+  printf("DEC_TEST_DROP_SPLIT value %u\nDEC_E_UNSUPPORTED value %d\n", DEC_TEST_DROP_SPLIT, DEC_E_UNSUPPORTED);
   printf("DEC_ERR_POS value %u\nDEC_ERR_TOKEN value %u\nDEC_ERR_SYNC value %u\n", DEC_ERR_POS, DEC_ERR_TOKEN,
          DEC_ERR_SYNC);
   printf("DEC_COUNTER_STRIDE value %d\n", DEC_COUNTER_STRIDE);
@@ -110,7 +115,11 @@ def test_struct_layout_matches_a_c_compiler(L, tmp_path):
         if field == "value":
             want = {"DEC_F32": L.DEC_F32, "DEC_BF16": L.DEC_BF16, "DEC_Q4": L.DEC_Q4,
                     "DEC_UNFUSED": L.DEC_UNFUSED, "DEC_NULL_KERNELS": L.DEC_NULL_KERNELS,
-                    "DEC_TEST_NO_WAIT": L.DEC_TEST_NO_WAIT,
+                    "DEC_TEST_NO_WAIT": L.DEC_TEST_NO_WAIT, "DEC_NO_FUSE_QKV": L.DEC_NO_FUSE_QKV,
+                    "DEC_NO_FUSE_FFN": L.DEC_NO_FUSE_FFN, "DEC_NO_FUSE_ATTN_O": L.DEC_NO_FUSE_ATTN_O,
+                    "DEC_DETERMINISTIC": L.DEC_DETERMINISTIC, "DEC_TEST_SKIP_ROPE": L.DEC_TEST_SKIP_ROPE,
+                    "DEC_TEST_APPEND_NEXT": L.DEC_TEST_APPEND_NEXT, "DEC_TEST_DROP_SPLIT": L.DEC_TEST_DROP_SPLIT,
+                    "DEC_E_UNSUPPORTED": E_UNSUPPORTED,
                     "DEC_ERR_POS": L.DEC_ERR_POS, "DEC_ERR_TOKEN": L.DEC_ERR_TOKEN, "DEC_ERR_SYNC": L.DEC_ERR_SYNC,
                     "DEC_E_NULL": E_NULL, "DEC_E_SHAPE": E_SHAPE, "DEC_E_DTYPE": E_DTYPE,
                     "DEC_E_ALIGN": E_ALIGN, "DEC_COUNTER_STRIDE": L.DEC_COUNTER_STRIDE}[name]
@@ -120,7 +129,7 @@ def test_struct_layout_matches_a_c_compiler(L, tmp_path):
         else:
             assert getattr(getattr(L, name), field).offset == val, f"{name}.{field}"
         seen += 1
-    assert seen == 51   # 4 sizes, 33 offsets, 14 constants
+    assert seen == 59   # 4 sizes, 33 offsets, 22 constants
 
 
 # ---- host-side checks (every call below is rejected before any launch)
@@ -214,6 +223,28 @@ def test_null_arguments_are_rejected(L):
     assert lib.dec_rope_table(1e4, 128, 16, None, None) == E_NULL
     assert lib.dec_embed(None, 32000, 4096, FAKE, FAKE, FAKE, None) == E_NULL
     assert lib.dec_advance(None, 0, 8, None, None, None) == E_NULL
+
+
+@pytest.mark.parametrize("flag", ["DEC_UNFUSED", "DEC_NO_FUSE_QKV", "DEC_NO_FUSE_FFN"])
+def test_per_op_paths_need_scratch(L, flag):
+    d = desc_of(L, synth.CONFIGS["C4"], flags=getattr(L, flag))
+    assert rc_step(L, d, weights_of(L), state_of(L)) == E_NULL and "scratch" in L.dec_last_error()
+
+
+def test_combine_in_output_projection_is_refused_where_it_does_not_apply(L):
+    """dec_attn_o_residual needs bf16 weights and cache and at most 32
+    attention splits, and cannot honour DEC_DETERMINISTIC (float atomics)."""
+    lib = L.load()
+    m = L.dec_mat(FAKE, None)
+    call = lambda d: lib.dec_attn_o_residual(ctypes.byref(d), m, ctypes.byref(state_of(L)), None)  # noqa: E731
+    assert call(desc_of(L, synth.CONFIGS["C1"])) == E_UNSUPPORTED          # f32 weights
+    assert call(desc_of(L, synth.CONFIGS["C4"], max_ctx=60000)) == E_UNSUPPORTED   # too many splits
+    assert "splits" in L.dec_last_error()
+    assert call(desc_of(L, synth.CONFIGS["C4"], flags=L.DEC_DETERMINISTIC)) == E_UNSUPPORTED
+    assert "atomics" in L.dec_last_error()
+    assert lib.dec_attn_o_residual(ctypes.byref(desc_of(L, synth.CONFIGS["C4"])), L.dec_mat(None, None),
+                                   ctypes.byref(state_of(L)), None) == E_NULL
+    assert lib.dec_attn_partials(ctypes.byref(desc_of(L, synth.CONFIGS["C4"])), None, None) == E_NULL
 
 
 def test_misaligned_pointers_are_rejected(L):

@@ -4,8 +4,8 @@ benchmark times (the same kernels, grids and split counts).
 * The first two layers of each 1B/7B/9B-shaped workload, at its real cache
   length, for three decode steps: every layer's output against the oracle
   run independently, and the cache slots the GPU wrote.
-* One decode token through the whole 40-layer 9B-shaped bf16 stack, layer by
-  layer.
+* One decode token through every layer of the 1B-, 7B-, 9B-shaped bf16 and
+  the 9B-shaped 4-bit stacks, layer by layer.
 * The five fused kernels against the ten per-op kernels at the 9B shapes
   (bf16 and 4-bit weights, real cache lengths): hidden states and caches
   equal bit for bit.
@@ -14,7 +14,8 @@ benchmark times (the same kernels, grids and split counts).
   greedy tokens stored under tests/golden/ (written by make_greedy.py, which
   calls only the oracle). A step may differ only where the oracle's top-2
   logit margin is below NEAR_TIE: there both tokens are correct to within
-  the arithmetic error, the runs part ways, and the comparison stops.
+  the arithmetic error; the oracle's token is fed back and all 64 steps are
+  compared.
 
 Tolerance: relative L2 of each layer's output <= 1e-4. The stated bound for
 bf16 and 4-bit workloads is 2e-2; every product here is exact (bf16 and
@@ -96,25 +97,38 @@ def test_first_layers_at_full_shape(gpu, name):
     _release()
 
 
-def test_whole_9b_stack_one_token(gpu):
-    cfg = synth.CONFIGS["C4"]
-    ora = oracle.Oracle.from_config(cfg, with_globals=False)
+@pytest.mark.parametrize("name", ["C2", "C3", "C4", "C5"])
+def test_whole_stack_one_token(gpu, name):
+    """One decode token at the first decode position through every layer of
+    the stack, each layer's output against the oracle. The oracle runs one
+    layer at a time on the GPU stack's own weights and prefill (each layer's
+    weights are drawn once, uploaded, used by the oracle and dropped), from
+    its own hidden state: no GPU value reaches it."""
+    cfg = synth.CONFIGS[name]
     st = DecodeStack(cfg)
-    for l in range(cfg.n_layers):
-        st.set_layer(l, ora.layers[l])
-        st.set_prefill(l, *synth.prefill(cfg, l))
     embed = synth.embedding(cfg)
     st.set_embedding(embed)
-    ora.glob = {"embed": embed}
     tok = int(synth.tokens(cfg)[0])
+    x = np.asarray(embed.data[tok], dtype=np.float32).astype(np.float64)
+    refs = [x]
+    for l in range(cfg.n_layers):
+        lw = synth.layer_weights(cfg, l)
+        pre = synth.prefill(cfg, l)
+        st.set_layer(l, lw)
+        st.set_prefill(l, *pre)
+        o = oracle.Oracle(cfg, [lw], keep_dequant=False)
+        o.load_prefill(0, *pre)
+        x = o.layer(0, x, cfg.ctx)
+        refs.append(x)
+        del o, lw, pre
     rec = torch.zeros(cfg.n_layers + 1, cfg.hidden, dtype=torch.float32, device="cuda")
     st.set_pos(cfg.ctx)
     st.set_token(tok)
     st.token_step(record=rec)
     got = rec.cpu().numpy()
-    ref = ora.step(tok, cfg.ctx)
-    errs = [rel_l2(got[l], ref[l]) for l in range(1, cfg.n_layers + 1)]
+    errs = [rel_l2(got[l], refs[l]) for l in range(1, cfg.n_layers + 1)]
     assert st.check_err() == 0
+    print(f"{name}: {cfg.n_layers} layers, worst relative L2 {max(errs):.2e} at layer {int(np.argmax(errs))}")
     assert max(errs) <= TOL, f"worst layer {int(np.argmax(errs))}: {max(errs):.3e}"
     _release()
 
@@ -196,13 +210,23 @@ def test_greedy_decode_matches_oracle(gpu, name):
     g = st.capture(cfg.ctx, cfg.ctx + cfg.steps, greedy=True)
     st.set_pos(cfg.ctx)
     st.set_token(gold["first_token"])
-    got = []
-    for _ in range(steps):
+    # every step is compared. Where the GPU's token differs from the oracle's,
+    # the oracle's top-2 margin must be below NEAR_TIE (both tokens are the
+    # argmax within the arithmetic error); the oracle's token is then written
+    # into the device token, so the run follows the oracle's sequence and the
+    # next step is compared on the same input.
+    exact, ties = 0, []
+    for s, want in enumerate(gold["tokens"][:steps]):
         g.replay()
-        got.append(int(st.token.item()))
+        got = int(st.token.item())
+        if got == want:
+            exact += 1
+            continue
+        assert gold["margins"][s] < NEAR_TIE, f"{name}: step {s} token {got} != {want} (margin {gold['margins'][s]:.3g})"
+        ties.append(s)
+        st.set_token(want)
     assert st.check_err() == 0
-    for s, (a, b) in enumerate(zip(got, gold["tokens"])):
-        if a != b:
-            assert gold["margins"][s] < NEAR_TIE, f"{name}: step {s} token {a} != {b} (margin {gold['margins'][s]:.3g})"
-            break
+    print(f"{name}: {exact} of {steps} greedy tokens equal, {len(ties)} near-tie steps {ties}")
+    assert exact + len(ties) == steps
+    assert len(ties) <= 2, f"{name}: {len(ties)} near-tie divergences"
     _release()

@@ -26,6 +26,8 @@ int launched(hipError_t e, const char* what) {
   return DEC_OK;
 }
 
+int64_t pad4(int64_t n) { return (n + 3) / 4 * 4; }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int ge_of(int wtype) { return wtype == DEC_F32 ? 4 : wtype == DEC_BF16 ? 8 : 32; }
@@ -80,6 +82,8 @@ dec::GemvArgs base_args(const dec_layer_desc* d) {
   a.max_ctx = d->max_ctx;
   a.kvtype = d->kvtype == DEC_BF16 ? 1 : 0;
   a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
+  a.fault = ((d->flags & DEC_TEST_SKIP_ROPE) ? dec::kFaultSkipRope : 0) |
+            ((d->flags & DEC_TEST_APPEND_NEXT) ? dec::kFaultAppendNext : 0);
   return a;
 }
 
@@ -120,19 +124,27 @@ int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t 
   a.kvtype = d->kvtype == DEC_BF16 ? 1 : 0;
   a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
   a.no_wait = (d->flags & DEC_TEST_NO_WAIT) ? 1 : 0;
+  a.drop_last = (d->flags & DEC_TEST_DROP_SPLIT) ? 1 : 0;
   a.partials_only = partials_only ? 1 : 0;
   dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
                  &a.chunk, &a.nsplit, &a.waves);
   return launched(dec::launch_attn(a, s), "attn_splitk");
 }
 
-// The fused layer combines attention inside the output projection for bf16
-// weights and cache when the split count allows it.
-bool attn_o_path(const dec_layer_desc* d) {
-  if (d->wtype != DEC_BF16 || d->kvtype != DEC_BF16 || (d->flags & DEC_TEST_NO_WAIT)) return false;
+// The combine inside the output projection: bf16 weights and cache and a
+// split count it supports.
+bool attn_o_possible(const dec_layer_desc* d) {
+  if (d->wtype != DEC_BF16 || d->kvtype != DEC_BF16) return false;
   int chunk, ns, nw;
   dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, 1, d->max_ctx, d->attn_chunk, &chunk, &ns, &nw);
   return dec::attn_o_supported(d->n_q_heads, d->n_kv_heads, d->head_dim, ns);
+}
+
+// The fused layer takes that path unless a flag turns it off (the failure
+// test of the in-kernel combine needs the in-kernel combine).
+bool attn_o_path(const dec_layer_desc* d) {
+  const uint32_t off = DEC_UNFUSED | DEC_NO_FUSE_ATTN_O | DEC_DETERMINISTIC | DEC_TEST_NO_WAIT;
+  return !(d->flags & off) && attn_o_possible(d);
 }
 
 int attn_o_launch(const dec_layer_desc* d, dec_mat wo, const dec_layer_state* st, hipStream_t s) {
@@ -149,6 +161,7 @@ int attn_o_launch(const dec_layer_desc* d, dec_mat wo, const dec_layer_state* st
   a.cols = d->n_q_heads * d->head_dim;
   a.max_ctx = d->max_ctx;
   a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
+  a.drop_last = (d->flags & DEC_TEST_DROP_SPLIT) ? 1 : 0;
   int nw;
   dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, 1, d->max_ctx, d->attn_chunk, &a.chunk, &a.nsplit, &nw);
   return launched(dec::launch_attn_o(a, s), "attn_o");
@@ -183,12 +196,70 @@ int ffn_launch(const dec_layer_desc* d, const void* norm, dec_mat wg, dec_mat wu
   return launched(gemv(d->wtype, dec::kEpiSwiglu, a, s), "gated_ffn");
 }
 
+// The first fused kernel as its four per-op kernels (rmsnorm, weight
+// multiply, QKV projection, RoPE + append), through `scratch`.
+int qkv_unfused(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st, hipStream_t s) {
+  const int H = d->hidden;
+  const int nullk = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
+  const int ntype = d->ntype == DEC_BF16 ? 1 : 0;
+  const int nqkv = (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+  float* u = st->scratch;
+  float* y = u + pad4(H);
+  int rc;
+  if ((rc = launched(dec::launch_rmsnorm_like(st->x, nullptr, ntype, u, H, d->rms_eps, d->wtype, 0, nullk, s),
+                     "rmsnorm")))
+    return rc;
+  if ((rc = launched(dec::launch_mul(u, w->attn_norm, ntype, H, nullk, s), "mul"))) return rc;
+  dec::GemvArgs a = base_args(d);
+  a.W = w->wqkv.w;
+  a.S = w->wqkv.scales;
+  a.rows = nqkv;
+  a.cols = H;
+  a.ntask = (nqkv + 1) / 2;
+  a.in = u;
+  a.y = y;
+  if ((rc = launched(gemv(d->wtype, dec::kEpiStore, a, s), "gemv_qkv"))) return rc;
+  return launched(dec::launch_rope_append(y, st->q, st->k_cache, st->v_cache, st->pos, st->rope, st->err,
+                                          d->n_q_heads, d->n_kv_heads, d->head_dim, d->max_ctx,
+                                          d->kvtype == DEC_BF16 ? 1 : 0, nullk, s),
+                  "rope_append");
+}
+
+// The gated FFN as its three per-op kernels (rmsnorm with multiply, gate/up
+// projection, SwiGLU), through `scratch`.
+int ffn_unfused(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st, hipStream_t s) {
+  const int H = d->hidden, F = d->ffn;
+  const int nullk = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
+  const int ntype = d->ntype == DEC_BF16 ? 1 : 0;
+  const int nqkv = (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+  float* u = st->scratch;
+  float* gate = u + pad4(H) + pad4(nqkv);
+  float* up = gate + pad4(F);
+  int rc;
+  if ((rc = launched(dec::launch_rmsnorm_like(st->x, w->ffn_norm, ntype, u, H, d->rms_eps, d->wtype, 1, nullk, s),
+                     "rmsnorm_mul")))
+    return rc;
+  dec::GemvArgs a = base_args(d);
+  a.W = w->wgate.w;
+  a.S = w->wgate.scales;
+  a.W2 = w->wup.w;
+  a.S2 = w->wup.scales;
+  a.rows = F;
+  a.cols = H;
+  a.ntask = F;
+  a.in = u;
+  a.y = gate;
+  a.y2 = up;
+  if ((rc = launched(gemv(d->wtype, dec::kEpiStore2, a, s), "gemv_gate_up"))) return rc;
+  return launched(dec::launch_swiglu(gate, up, st->h, F, nullk, s), "swiglu");
+}
+
 int check_state(const dec_layer_state* st, bool scratch) {
   if (!st) return fail(DEC_E_NULL, "state is NULL");
   if (!st->x || !st->q || !st->attn || !st->h || !st->part || !st->counters || !st->k_cache ||
       !st->v_cache || !st->pos || !st->rope || !st->err)
     return fail(DEC_E_NULL, "a state pointer is NULL");
-  if (scratch && !st->scratch) return fail(DEC_E_NULL, "scratch is NULL (needed by DEC_UNFUSED)");
+  if (scratch && !st->scratch) return fail(DEC_E_NULL, "scratch is NULL (needed by DEC_UNFUSED, DEC_NO_FUSE_QKV, DEC_NO_FUSE_FFN)");
   for (const void* p : {(const void*)st->x, (const void*)st->q, (const void*)st->attn,
                         (const void*)st->h, (const void*)st->part, (const void*)st->k_cache,
                         (const void*)st->v_cache})
@@ -207,8 +278,6 @@ int check_weights(const dec_layer_desc* d, const dec_layer_weights* w) {
     return rc;
   return DEC_OK;
 }
-
-int64_t pad4(int64_t n) { return (n + 3) / 4 * 4; }
 
 }  // namespace
 
@@ -248,6 +317,23 @@ int dec_attn_splitk(const dec_layer_desc* d, const dec_layer_state* st, void* st
   return attn_launch(d, st, hipStream_t(stream));
 }
 
+int dec_attn_partials(const dec_layer_desc* d, const dec_layer_state* st, void* stream) {
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_state(st, false))) return rc;
+  return attn_launch(d, st, hipStream_t(stream), true);
+}
+
+int dec_attn_o_residual(const dec_layer_desc* d, dec_mat wo, const dec_layer_state* st, void* stream) {
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_state(st, false)) || (rc = check_mat(d, wo, "wo"))) return rc;
+  if (d->flags & DEC_DETERMINISTIC)
+    return fail(DEC_E_UNSUPPORTED, "the combine inside the output projection adds with float atomics");
+  if (!attn_o_possible(d))
+    return fail(DEC_E_UNSUPPORTED, "needs bf16 weights and cache and at most %d attention splits",
+                dec::kAttnOSplits);
+  return attn_o_launch(d, wo, st, hipStream_t(stream));
+}
+
 int dec_gemv_residual(const dec_layer_desc* d, dec_mat w, int32_t rows, int32_t cols,
                       const float* in, float* x, void* stream) {
   int rc;
@@ -276,70 +362,22 @@ int dec_gated_ffn(const dec_layer_desc* d, const void* ffn_norm, dec_mat wgate, 
 int dec_layer_step(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st,
                    void* stream) {
   int rc;
-  const bool unfused = d && (d->flags & DEC_UNFUSED);
-  if ((rc = check_desc(d)) || (rc = check_weights(d, w)) || (rc = check_state(st, unfused))) return rc;
+  const uint32_t f = d ? d->flags : 0u;
+  const bool split_qkv = f & (DEC_UNFUSED | DEC_NO_FUSE_QKV);
+  const bool split_ffn = f & (DEC_UNFUSED | DEC_NO_FUSE_FFN);
+  if ((rc = check_desc(d)) || (rc = check_weights(d, w)) || (rc = check_state(st, split_qkv || split_ffn))) return rc;
   hipStream_t s = hipStream_t(stream);
   const int H = d->hidden, F = d->ffn, qd = d->n_q_heads * d->head_dim;
-  if (!unfused) {
-    if ((rc = qkv_launch(d, w, st, s))) return rc;
-    if (attn_o_path(d)) {
-      if ((rc = attn_launch(d, st, s, true))) return rc;
-      if ((rc = attn_o_launch(d, w->wo, st, s))) return rc;
-    } else {
-      if ((rc = attn_launch(d, st, s))) return rc;
-      if ((rc = residual_launch(d, w->wo, H, qd, st->attn, st->x, s))) return rc;
-    }
-    if ((rc = ffn_launch(d, w->ffn_norm, w->wgate, w->wup, st->x, st->h, s))) return rc;
-    return residual_launch(d, w->wdown, H, F, st->h, st->x, s);
+  if ((rc = split_qkv ? qkv_unfused(d, w, st, s) : qkv_launch(d, w, st, s))) return rc;
+  if (attn_o_path(d)) {
+    if ((rc = attn_launch(d, st, s, true))) return rc;
+    if ((rc = attn_o_launch(d, w->wo, st, s))) return rc;
+  } else {
+    if ((rc = attn_launch(d, st, s))) return rc;
+    if ((rc = residual_launch(d, w->wo, H, qd, st->attn, st->x, s))) return rc;
   }
-  // The ten per-op kernels of the same arithmetic: rmsnorm, weight multiply,
-  // QKV projection, RoPE + append, attention, output projection + residual,
-  // rmsnorm with multiply, gate/up projection, SwiGLU, down projection +
-  // residual. Intermediates go through `scratch`.
-  const int nullk = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
-  const int ntype = d->ntype == DEC_BF16 ? 1 : 0;
-  const int nqkv = (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
-  float* u = st->scratch;
-  float* y = u + pad4(H);
-  float* gate = y + pad4(nqkv);
-  float* up = gate + pad4(F);
-  if ((rc = launched(dec::launch_rmsnorm_like(st->x, nullptr, ntype, u, H, d->rms_eps, d->wtype, 0, nullk, s),
-                     "rmsnorm")))
+  if ((rc = split_ffn ? ffn_unfused(d, w, st, s) : ffn_launch(d, w->ffn_norm, w->wgate, w->wup, st->x, st->h, s)))
     return rc;
-  if ((rc = launched(dec::launch_mul(u, w->attn_norm, ntype, H, nullk, s), "mul"))) return rc;
-  dec::GemvArgs a = base_args(d);
-  a.W = w->wqkv.w;
-  a.S = w->wqkv.scales;
-  a.rows = nqkv;
-  a.cols = H;
-  a.ntask = (nqkv + 1) / 2;
-  a.in = u;
-  a.y = y;
-  if ((rc = launched(gemv(d->wtype, dec::kEpiStore, a, s), "gemv_qkv"))) return rc;
-  if ((rc = launched(dec::launch_rope_append(y, st->q, st->k_cache, st->v_cache, st->pos, st->rope, st->err,
-                                             d->n_q_heads, d->n_kv_heads, d->head_dim, d->max_ctx,
-                                             d->kvtype == DEC_BF16 ? 1 : 0, nullk, s),
-                     "rope_append")))
-    return rc;
-  if ((rc = attn_launch(d, st, s))) return rc;
-  if ((rc = residual_launch(d, w->wo, H, qd, st->attn, st->x, s))) return rc;
-  if ((rc = launched(dec::launch_rmsnorm_like(st->x, w->ffn_norm, ntype, u, H, d->rms_eps, d->wtype, 1, nullk,
-                                              s),
-                     "rmsnorm_mul")))
-    return rc;
-  a = base_args(d);
-  a.W = w->wgate.w;
-  a.S = w->wgate.scales;
-  a.W2 = w->wup.w;
-  a.S2 = w->wup.scales;
-  a.rows = F;
-  a.cols = H;
-  a.ntask = F;
-  a.in = u;
-  a.y = gate;
-  a.y2 = up;
-  if ((rc = launched(gemv(d->wtype, dec::kEpiStore2, a, s), "gemv_gate_up"))) return rc;
-  if ((rc = launched(dec::launch_swiglu(gate, up, st->h, F, nullk, s), "swiglu"))) return rc;
   return residual_launch(d, w->wdown, H, F, st->h, st->x, s);
 }
 

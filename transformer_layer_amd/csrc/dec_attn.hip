@@ -274,6 +274,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   if (w == kNotCombiner) return;
 
   if (w >= 0) {
+    // (drop_last, tests of the parity gates: the last split is left out)
+    const int nsum = a.drop_last && ns > 1 ? ns - 1 : ns;
     const float* pj = a.part + size_t(j) * a.nsplit * G * D;
     const float* mlj = a.part + size_t(a.nkv) * a.nsplit * G * D + size_t(j) * a.nsplit * G * 2;
     // this combiner's slice of the float4 outputs; `parts` threads share an
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int k = 0; k < kPre; ++k) {
       const int t = part + k * parts;
       pre[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (active && t < ns) {
+      if (active && t < nsum) {
         const float* pv = pj + size_t(t) * G * D + f * 4;
         const float2 lo = load_pair_agent(pv), hi = load_pair_agent(pv + 2);
         pre[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int k = 0; k < kSplitMax / kWave; ++k) {
         const int t = lane + k * kWave;
-        ml[k] = t < ns ? load_pair_agent(mlj + (t * G + hh) * 2) : make_float2(-INFINITY, 0.0f);
+        ml[k] = t < nsum ? load_pair_agent(mlj + (t * G + hh) * 2) : make_float2(-INFINITY, 0.0f);
         M = fmaxf(M, ml[k].x);
       }
       M = wave_max(M);
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int k = 0; k < kSplitMax / kWave; ++k) {
         const int t = lane + k * kWave;
-        if (t < ns) {
+        if (t < nsum) {
           const float wt = exp2f(ml[k].x - M);
           wts[t][hh] = wt;
           dsum = fmaf(wt, ml[k].y, dsum);
@@ -334,11 +336,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int k = 0; k < kPre; ++k) {
         const int t = part + k * parts;
-        const float wt = t < ns ? wts[t][hh] : 0.0f;
+        const float wt = t < nsum ? wts[t][hh] : 0.0f;
         acc.x = fmaf(pre[k].x, wt, acc.x); acc.y = fmaf(pre[k].y, wt, acc.y);
         acc.z = fmaf(pre[k].z, wt, acc.z); acc.w = fmaf(pre[k].w, wt, acc.w);
       }
-      for (int t = part + kPre * parts; t < ns; t += parts) {
+      for (int t = part + kPre * parts; t < nsum; t += parts) {
         const float* pv = pj + size_t(t) * G * D + f * 4;
         const float2 lo = load_pair_agent(pv), hi = load_pair_agent(pv + 2);
         const float wt = wts[t][hh];

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(512) void attn_o_kernel(AttnOArgs a) {
   }
 
   // this workgroup's Wo rows: lane (sub, li) of wave wv takes rows
-  // r0 + wv*NL*RPW + u*RPW + sub, columns j*C + li*8 .. +7
+  // r0 + wv*NL*RPW + u*RPW + sub, columns c0 + li*8 .. +7 (c0 = cb*C)
   const int sub = lane / LPR, li = lane % LPR;
   const int r0 = rb * R + wv * NL * RPW + sub;
   const uint8_t* W = reinterpret_cast<const uint8_t*>(a.W);
@@ -82,7 +82,8 @@ __global__ __launch_bounds__(512) void attn_o_kernel(AttnOArgs a) {
   // the position decides which splits hold cache rows
   const int pos = *a.pos;
   if (pos < 0 || pos >= a.max_ctx) return;   // the attention kernel flagged it and wrote nothing
-  const int ns = (pos + a.chunk) / a.chunk;  // splits over positions 0..pos
+  int ns = (pos + a.chunk) / a.chunk;        // splits over positions 0..pos
+  if (a.drop_last && ns > 1) --ns;           // (tests of the parity gates: the last split left out)
 
   __shared__ float wts[8][kAttnOSplits];      // per head and split: exp2(m - M) / den
   __shared__ float4 red[NT];

@@ -159,14 +159,15 @@ struct PairEpi {
       const int half = a.d / 2;
       const int head = p / half;
       const int i = p % half;
-      if (head < a.nq + a.nkv) rope_rotate(y0, y1, e0, e1);
+      if (head < a.nq + a.nkv && !(a.fault & kFaultSkipRope)) rope_rotate(y0, y1, e0, e1);
       if (head < a.nq) {
         a.y[r0] = y0;
         a.y[r1] = y1;
       } else {
         const bool isk = head < a.nq + a.nkv;
         const int j = isk ? head - a.nq : head - a.nq - a.nkv;
-        const size_t off = (size_t(j) * a.max_ctx + pos) * a.d + i;
+        const int slot = (a.fault & kFaultAppendNext) && pos + 1 < a.max_ctx ? pos + 1 : pos;
+        const size_t off = (size_t(j) * a.max_ctx + slot) * a.d + i;
         void* cache = isk ? a.kc : a.vc;
         if (a.kvtype == 1) {
           uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);

@@ -11,24 +11,29 @@ static hipError_t go_q4mfma(const GemvArgs& a, int ntiles, hipStream_t s) {
   // each re-quantizes the input once for three tiles, +0.15% tokens/s in a
   // same-box A/B; each tile's weights are still requested only once the
   // previous tile runs: requesting the second and third together lost 3.5%)
+  // (16 steps per wave, rows above 12288 columns: one tile per workgroup,
+  // since two tiles' weights in flight would not fit in registers)
+  constexpr bool kMulti = SPW <= 12;
   auto one = q4mfma_kernel<EPI, NW, SPW, 1>;
   const int lds1 = q4mfma_lds_bytes(a.cols, NW, SPW, 1);
   const int lds2 = q4mfma_lds_bytes(a.cols, NW, SPW, 2);
   const int lds3 = q4mfma_lds_bytes(a.cols, NW, SPW, 3);
   if (lds1 > 65536) return hipErrorInvalidValue;
-  if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_SWIGLU && kMulti) {
     if (ntiles >= 1536 && lds3 <= 65536) {
       auto three = q4mfma_kernel<EPI, NW, SPW, 3>;
       hipLaunchKernelGGL(three, dim3((ntiles + 2) / 3), dim3(NW * 64), lds3, s, a);
       return hipGetLastError();
     }
   }
-  if (ntiles <= resident_blocks(one, NW * 64, lds1) || lds2 > 65536) {
-    hipLaunchKernelGGL(one, dim3(ntiles), dim3(NW * 64), lds1, s, a);
-  } else {
-    auto two = q4mfma_kernel<EPI, NW, SPW, 2>;
-    hipLaunchKernelGGL(two, dim3((ntiles + 1) / 2), dim3(NW * 64), lds2, s, a);
+  if constexpr (kMulti) {
+    if (ntiles > resident_blocks(one, NW * 64, lds1) && lds2 <= 65536) {
+      auto two = q4mfma_kernel<EPI, NW, SPW, 2>;
+      hipLaunchKernelGGL(two, dim3((ntiles + 1) / 2), dim3(NW * 64), lds2, s, a);
+      return hipGetLastError();
+    }
   }
+  hipLaunchKernelGGL(one, dim3(ntiles), dim3(NW * 64), lds1, s, a);
   return hipGetLastError();
 }
 

@@ -11,6 +11,12 @@ constexpr uint32_t kErrToken = 0x2u;
 constexpr uint32_t kErrSync = 0x4u;
 constexpr int kCounterStride = 16;  // uint32 words between two kv heads' arrival counters (64 bytes)
 
+// Test-only arithmetic faults of the QKV epilogue (GemvArgs::fault): the
+// kernels still run to completion and store in bounds, but the numbers are
+// wrong, so a parity test must fail under each.
+constexpr int kFaultSkipRope = 0x1;    // q and k left unrotated
+constexpr int kFaultAppendNext = 0x2;  // k, v stored at position pos + 1 (pos itself when pos + 1 is past the cache)
+
 // Arguments of the GEMV-core kernels (passed by value).
 struct GemvArgs {
   const void* W;       // first matrix (elements)
@@ -35,6 +41,7 @@ struct GemvArgs {
   void* vc;
   uint32_t* err;
   int null_kernel;
+  int fault;           // kFault* bits (tests of the parity gates only)
 };
 
 // Granules (16-byte weight groups) per lane for a row of `cols` elements
@@ -83,7 +90,7 @@ struct AttnArgs {
   const float* q;      // [n_q d]
   const void* kc;      // [n_kv][max_ctx][d]
   const void* vc;
-  float* part;         // [n_kv][S][g][d + 2]
+  float* part;         // o [n_kv][S][g][d], then (m, l) [n_kv][S][g][2]
   uint32_t* counters;  // [n_kv * kCounterStride]
   float* out;          // [n_q d]
   const int32_t* pos;
@@ -92,6 +99,7 @@ struct AttnArgs {
   int waves;           // waves per workgroup (4 or 8)
   int no_wait;         // combiners give up at once when splits are missing (failure-path tests)
   int partials_only;   // write the splits' partials and stop (the output projection combines them)
+  int drop_last;       // test-only fault: the combine leaves out the last split (two or more splits)
   int null_kernel;
 };
 
@@ -109,6 +117,7 @@ struct AttnOArgs {
   float* x;            // [rows], updated with float atomics
   const int32_t* pos;
   int nq, nkv, d, rows, cols, nsplit, chunk, max_ctx;
+  int drop_last;       // test-only fault: the combine leaves out the last split (two or more splits)
   int null_kernel;
 };
 bool attn_o_supported(int n_q, int n_kv, int head_dim, int nsplit);

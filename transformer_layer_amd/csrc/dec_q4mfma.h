@@ -201,7 +201,6 @@ template <int EPI, int NW, int SPW, int TT>
 __global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
   using PE = PairEpi<EPI>;
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_NORM_STORE);
-  constexpr int NT = NW * 64;
   static_assert(NW >= 4, "the sum of squares uses the first four waves");
   extern __shared__ __align__(16) uint8_t smem[];
 
@@ -223,7 +222,6 @@ __global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
 
   const size_t row_bytes = size_t(a.cols) / 2;
   const int npairs = PE::npairs(a);
-  const int ntiles = (npairs + 7) / 8;
   const int s0 = wv * SPW;
   const int ns = max(0, min(S - s0, SPW));   // steps of this wave (wave-uniform)
 

@@ -16,11 +16,18 @@ DEC_F32, DEC_BF16, DEC_Q4 = 0, 1, 2
 DTYPES = {"f32": DEC_F32, "bf16": DEC_BF16, "q4": DEC_Q4}
 DEC_UNFUSED = 0x1
 DEC_NULL_KERNELS = 0x2
+DEC_NO_FUSE_QKV = 0x4
+DEC_NO_FUSE_FFN = 0x8
+DEC_NO_FUSE_ATTN_O = 0x10
+DEC_DETERMINISTIC = 0x20
 DEC_TEST_NO_WAIT = 0x100
+DEC_TEST_SKIP_ROPE = 0x200
+DEC_TEST_APPEND_NEXT = 0x400
+DEC_TEST_DROP_SPLIT = 0x800
 DEC_ERR_POS = 0x1
 DEC_ERR_TOKEN = 0x2
 DEC_ERR_SYNC = 0x4
-ABI_VERSION = 2
+ABI_VERSION = 3
 DEC_COUNTER_STRIDE = 16
 
 c_void_p, c_int32, c_uint32, c_float, c_double, c_int64 = (
@@ -60,6 +67,8 @@ SIGNATURES = {
     "dec_scratch_floats": (c_int64, [P_DESC]),
     "dec_rmsnorm_gemv_qkv_rope": (ctypes.c_int, [P_DESC, P_W, P_ST, c_void_p]),
     "dec_attn_splitk": (ctypes.c_int, [P_DESC, P_ST, c_void_p]),
+    "dec_attn_partials": (ctypes.c_int, [P_DESC, P_ST, c_void_p]),
+    "dec_attn_o_residual": (ctypes.c_int, [P_DESC, dec_mat, P_ST, c_void_p]),
     "dec_gemv_residual": (ctypes.c_int, [P_DESC, dec_mat, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "dec_gated_ffn": (ctypes.c_int, [P_DESC, c_void_p, dec_mat, dec_mat, c_void_p, c_void_p, c_void_p]),
     "dec_layer_step": (ctypes.c_int, [P_DESC, P_W, P_ST, c_void_p]),
@@ -140,6 +149,15 @@ def dec_rmsnorm_gemv_qkv_rope(desc, weights, state, stream=None) -> None:
 
 def dec_attn_splitk(desc, state, stream=None) -> None:
     _check(load().dec_attn_splitk(ctypes.byref(desc), ctypes.byref(state), _s(stream)), "dec_attn_splitk")
+
+
+def dec_attn_partials(desc, state, stream=None) -> None:
+    _check(load().dec_attn_partials(ctypes.byref(desc), ctypes.byref(state), _s(stream)), "dec_attn_partials")
+
+
+def dec_attn_o_residual(desc, wo: dec_mat, state, stream=None) -> None:
+    _check(load().dec_attn_o_residual(ctypes.byref(desc), wo, ctypes.byref(state), _s(stream)),
+           "dec_attn_o_residual")
 
 
 def dec_gemv_residual(desc, w: dec_mat, rows: int, cols: int, inp: int, x: int, stream=None) -> None:
