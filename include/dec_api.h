@@ -277,6 +277,29 @@ int dec_gated_ffn(const dec_layer_desc* desc, const void* ffn_norm, dec_mat wgat
 int dec_layer_step(const dec_layer_desc* desc, const dec_layer_weights* w,
                    const dec_layer_state* st, void* stream);
 
+/* ---- the same step without caller-provided scratch ----------------------- */
+
+/* Bytes of the library's static device scratch (per GPU, held until the
+   process ends). */
+#define DEC_STATIC_SCRATCH_BYTES (4u << 20)
+
+/* dec_layer_step for callers that cannot allocate device memory: code under
+   HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+   The attention's split partials, its arrival counters and the per-op
+   intermediates live in a static device array of the library instead of
+   st->part, st->counters and st->scratch, which are not read (they may be
+   NULL); every other field of st is used as in dec_layer_step. The array
+   holds DEC_STATIC_SCRATCH_BYTES per GPU: a shape whose 64 KiB of counter
+   words, partials (dec_attn_part_floats) and per-op intermediates
+   (dec_scratch_floats, floats) do not fit returns DEC_E_SHAPE. The first
+   call on a GPU looks up the array's address there and enqueues a clear of
+   the counters on `stream`; nothing is allocated, copied or synchronized.
+   Every call on one GPU shares that GPU's array, which keeps the last call's
+   contents, so calls that overlap on one GPU (other streams, other threads)
+   race and must be serialized by the caller. */
+int dec_layer_step_static(const dec_layer_desc* desc, const dec_layer_weights* w,
+                          const dec_layer_state* st, void* stream);
+
 /* ---- LM head ------------------------------------------------------------- */
 
 /* Final RMSNorm, LM head and greedy choice of the next token: the "LM head +

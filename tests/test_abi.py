@@ -247,6 +247,23 @@ def test_combine_in_output_projection_is_refused_where_it_does_not_apply(L):
     assert lib.dec_attn_partials(ctypes.byref(desc_of(L, synth.CONFIGS["C4"])), None, None) == E_NULL
 
 
+def test_static_step_rejects_shapes_beyond_its_scratch(L):
+    """dec_layer_step_static checks its scratch capacity before touching the
+    device: a cache long enough that the split partials pass
+    DEC_STATIC_SCRATCH_BYTES is refused with DEC_E_SHAPE."""
+    lib = L.load()
+    cfg = synth.CONFIGS["C4"]
+    ctx = cfg.max_ctx
+    while 4 * L.dec_attn_part_floats(desc_of(L, cfg, max_ctx=ctx)) + (64 << 10) <= L.DEC_STATIC_SCRATCH_BYTES:
+        ctx *= 2
+    d = desc_of(L, cfg, max_ctx=ctx)
+    st = state_of(L, part=None, counters=None)
+    assert lib.dec_layer_step_static(ctypes.byref(d), ctypes.byref(weights_of(L)), ctypes.byref(st), None) == E_SHAPE
+    assert "static scratch" in L.dec_last_error()
+    assert lib.dec_layer_step_static(ctypes.byref(d), ctypes.byref(weights_of(L)), None, None) == E_NULL
+    assert lib.dec_layer_step_static(None, ctypes.byref(weights_of(L)), ctypes.byref(st), None) == E_NULL
+
+
 def test_misaligned_pointers_are_rejected(L):
     d = desc_of(L, synth.CONFIGS["C4"])
     bad = L.dec_mat(FAKE + 2, None)
@@ -306,7 +323,10 @@ def test_library_allocates_copies_and_synchronises_nothing(L):
     allowed = {"__hipRegisterFatBinary", "__hipUnregisterFatBinary", "__hipRegisterFunction",
                "__hipRegisterVar", "__hipPushCallConfiguration", "__hipPopCallConfiguration",
                "hipLaunchKernel", "hipGetDevice", "hipDeviceGetAttribute", "hipGetLastError",
-               "hipGetErrorString", "hipOccupancyMaxActiveBlocksPerMultiprocessor"}
+               "hipGetErrorString", "hipOccupancyMaxActiveBlocksPerMultiprocessor",
+               # dec_layer_step_static: its array's device address, and whether the
+               # caller's stream is capturing (a query, no work enqueued)
+               "hipGetSymbolAddress", "hipStreamIsCapturing"}
     assert hip <= allowed, f"unexpected HIP runtime imports: {sorted(hip - allowed)}"
     assert not {s for s in imported if s in ("malloc", "calloc", "realloc") or "Malloc" in s}, \
         "the library should not allocate host memory either"

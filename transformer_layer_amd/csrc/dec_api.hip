@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dec_api.h"
 #include "dec_internal.h"
@@ -279,6 +280,55 @@ int check_weights(const dec_layer_desc* d, const dec_layer_weights* w) {
   return DEC_OK;
 }
 
+// ---- the library's own scratch (dec_layer_step_static): attention arrival
+// counters at offset 0, split partials from kStaticPartOffset, per-op
+// intermediates after them. A file-scope device array: every GPU the library
+// runs on holds its own copy until the process ends. Host code must not pass
+// `scratch` itself to a kernel (on the host it is a stand-in, not a device
+// address): the address comes from hipGetSymbolAddress, per device.
+constexpr size_t kStaticBytes = DEC_STATIC_SCRATCH_BYTES;
+constexpr size_t kStaticCounterWords = 16384;                 // 256 kv heads x DEC_COUNTER_STRIDE
+constexpr size_t kStaticPartOffset = kStaticCounterWords * 4;   // 64 KiB
+static __device__ __align__(256) uint8_t scratch[kStaticBytes];
+
+__global__ void clear_words(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_addr[kMaxDevices];      // the array's address on each device (null: not looked up yet)
+bool g_static_cleared[kMaxDevices];    // counters cleared by a launch that has run outside a capture
+
+// The array's address on the current device, looked up once per device;
+// the first call enqueues a clear of the counter words on `s` (a kernel, not
+// a memset, so that a capturing caller records it as an ordinary node).
+int static_scratch(hipStream_t s, uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(DEC_E_LAUNCH, "no current device for the static scratch");
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(DEC_E_LAUNCH, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_static_addr[dev] = p;
+  }
+  uint8_t* base = static_cast<uint8_t*>(g_static_addr[dev]);
+  if (!g_static_cleared[dev]) {
+    hipLaunchKernelGGL(clear_words, dim3(64), dim3(256), 0, s, reinterpret_cast<uint32_t*>(base),
+                       int(kStaticCounterWords));
+    int rc;
+    if ((rc = launched(hipGetLastError(), "clear static counters"))) return rc;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) g_static_cleared[dev] = true;
+  }
+  *out = base;
+  return DEC_OK;
+}
+
+int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
+
 }  // namespace
 
 extern "C" {
@@ -379,6 +429,27 @@ int dec_layer_step(const dec_layer_desc* d, const dec_layer_weights* w, const de
   if ((rc = split_ffn ? ffn_unfused(d, w, st, s) : ffn_launch(d, w->ffn_norm, w->wgate, w->wup, st->x, st->h, s)))
     return rc;
   return residual_launch(d, w->wdown, H, F, st->h, st->x, s);
+}
+
+int dec_layer_step_static(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st,
+                          void* stream) {
+  int rc;
+  if ((rc = check_desc(d))) return rc;
+  if (!st) return fail(DEC_E_NULL, "state is NULL");
+  const int64_t part = pad64(dec_attn_part_floats(d));
+  const int64_t ops = dec_scratch_floats(d);
+  if (int64_t(d->n_kv_heads) * DEC_COUNTER_STRIDE > int64_t(kStaticCounterWords) ||
+      int64_t(kStaticPartOffset) + 4 * (part + ops) > int64_t(kStaticBytes))
+    return fail(DEC_E_SHAPE, "static scratch of %zu bytes is too small: %lld partial and %lld per-op floats",
+                kStaticBytes, (long long)part, (long long)ops);
+  hipStream_t s = hipStream_t(stream);
+  uint8_t* base = nullptr;
+  if ((rc = static_scratch(s, &base))) return rc;
+  dec_layer_state in = *st;
+  in.counters = reinterpret_cast<uint32_t*>(base);
+  in.part = reinterpret_cast<float*>(base + kStaticPartOffset);
+  in.scratch = in.part + part;
+  return dec_layer_step(d, w, &in, stream);
 }
 
 int dec_lm_head(const dec_layer_desc* d, int32_t head_type, const void* final_norm, dec_mat head,

@@ -29,6 +29,7 @@ DEC_ERR_TOKEN = 0x2
 DEC_ERR_SYNC = 0x4
 ABI_VERSION = 3
 DEC_COUNTER_STRIDE = 16
+DEC_STATIC_SCRATCH_BYTES = 4 << 20
 
 c_void_p, c_int32, c_uint32, c_float, c_double, c_int64 = (
     ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_double, ctypes.c_int64)
@@ -72,6 +73,7 @@ SIGNATURES = {
     "dec_gemv_residual": (ctypes.c_int, [P_DESC, dec_mat, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "dec_gated_ffn": (ctypes.c_int, [P_DESC, c_void_p, dec_mat, dec_mat, c_void_p, c_void_p, c_void_p]),
     "dec_layer_step": (ctypes.c_int, [P_DESC, P_W, P_ST, c_void_p]),
+    "dec_layer_step_static": (ctypes.c_int, [P_DESC, P_W, P_ST, c_void_p]),
     "dec_lm_head": (ctypes.c_int, [P_DESC, c_int32, c_void_p, dec_mat, c_int32, c_void_p, c_void_p, c_void_p,
                                     c_void_p]),
     "dec_rope_table": (ctypes.c_int, [c_double, c_int32, c_int32, c_void_p, c_void_p]),
@@ -171,6 +173,11 @@ def dec_gated_ffn(desc, ffn_norm: int, wgate: dec_mat, wup: dec_mat, x: int, h: 
 def dec_layer_step(desc, weights, state, stream=None) -> None:
     _check(load().dec_layer_step(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(state),
                                  _s(stream)), "dec_layer_step")
+
+
+def dec_layer_step_static(desc, weights, state, stream=None) -> None:
+    _check(load().dec_layer_step_static(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(state),
+                                        _s(stream)), "dec_layer_step_static")
 
 
 def dec_lm_head(desc, head_type: int, final_norm: int, head: dec_mat, vocab: int, x: int, logits: int,
