@@ -252,7 +252,8 @@ def test_static_step_rejects_shapes_beyond_its_scratch(L):
     device: a cache long enough that the split partials pass
     DEC_STATIC_SCRATCH_BYTES is refused with DEC_E_SHAPE."""
     lib = L.load()
-    cfg = synth.CONFIGS["C4"]
+    # 128 query heads: each split's partials take 128 x 130 floats
+    cfg = synth.CONFIGS["C4"].with_(hidden=16384, n_q_heads=128, n_kv_heads=16, ffn=16384)
     ctx = cfg.max_ctx
     while 4 * L.dec_attn_part_floats(desc_of(L, cfg, max_ctx=ctx)) + (64 << 10) <= L.DEC_STATIC_SCRATCH_BYTES:
         ctx *= 2

@@ -50,9 +50,9 @@ int check_desc(const dec_layer_desc* d) {
   if (d->max_ctx <= 0 || d->max_ctx > (1 << 20)) return fail(DEC_E_SHAPE, "max_ctx %d", d->max_ctx);
   if (!(d->rms_eps >= 0.0f)) return fail(DEC_E_SHAPE, "rms_eps");
   if (d->attn_chunk < 0 || d->attn_chunk > 256) return fail(DEC_E_SHAPE, "attn_chunk %d (0..256)", d->attn_chunk);
-  int chunk, ns, nw;
+  int chunk, ns, nw, lds;
   dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
-                 &chunk, &ns, &nw);
+                 &chunk, &ns, &nw, &lds);
   if (ns > 256) return fail(DEC_E_SHAPE, "max_ctx %d needs %d splits (max 256)", d->max_ctx, ns);
   return DEC_OK;
 }
@@ -128,7 +128,7 @@ int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t 
   a.drop_last = (d->flags & DEC_TEST_DROP_SPLIT) ? 1 : 0;
   a.partials_only = partials_only ? 1 : 0;
   dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
-                 &a.chunk, &a.nsplit, &a.waves);
+                 &a.chunk, &a.nsplit, &a.waves, &a.lds);
   return launched(dec::launch_attn(a, s), "attn_splitk");
 }
 
@@ -136,8 +136,8 @@ int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t 
 // split count it supports.
 bool attn_o_possible(const dec_layer_desc* d) {
   if (d->wtype != DEC_BF16 || d->kvtype != DEC_BF16) return false;
-  int chunk, ns, nw;
-  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, 1, d->max_ctx, d->attn_chunk, &chunk, &ns, &nw);
+  int chunk, ns, nw, lds;
+  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, 1, d->max_ctx, d->attn_chunk, &chunk, &ns, &nw, &lds);
   return dec::attn_o_supported(d->n_q_heads, d->n_kv_heads, d->head_dim, ns);
 }
 
@@ -163,8 +163,9 @@ int attn_o_launch(const dec_layer_desc* d, dec_mat wo, const dec_layer_state* st
   a.max_ctx = d->max_ctx;
   a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
   a.drop_last = (d->flags & DEC_TEST_DROP_SPLIT) ? 1 : 0;
-  int nw;
-  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, 1, d->max_ctx, d->attn_chunk, &a.chunk, &a.nsplit, &nw);
+  int nw, lds;
+  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, 1, d->max_ctx, d->attn_chunk, &a.chunk, &a.nsplit, &nw,
+                 &lds);
   return launched(dec::launch_attn_o(a, s), "attn_o");
 }
 
@@ -339,9 +340,9 @@ const char* dec_last_error(void) { return g_err; }
 
 int64_t dec_attn_part_floats(const dec_layer_desc* d) {
   if (check_desc(d)) return -1;
-  int chunk, ns, nw;
+  int chunk, ns, nw, lds;
   dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
-                 &chunk, &ns, &nw);
+                 &chunk, &ns, &nw, &lds);
   return int64_t(d->n_q_heads) * ns * (d->head_dim + 2);
 }
 

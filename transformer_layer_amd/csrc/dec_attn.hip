@@ -14,56 +14,10 @@
 // during the softmax. With a single row step the scores are too short to
 // cover V's latency, and V is requested right after K.
 //
-// The last workgroups of a kv head to arrive (one per ~8 KB of partials, at
-// most kCombiners) combine its partials with a log-sum-exp rescale, each a
-// slice of the head group's outputs (one workgroup alone fetches the partials
-// too slowly). Ordering without an L2
-// write-back: the partials are written with agent-scope atomic stores, which
-// reach the device-coherent level by themselves; every lane waits until its
-// stores have completed (vmcnt 0), the workgroup meets at a barrier, and one
-// thread increments the head's arrival counter with an agent-scope atomic.
-// Combiners that arrive before the last one poll that counter (bounded: on
-// giving up they set DEC_ERR_SYNC and write nothing) and read the partials
-// with agent-scope loads. Every counter line is 64 bytes, so the heads'
-// arrivals do not queue on one line; the last combiner to finish resets the
-// line, so the kernel replays unchanged inside a graph.
-#include "dec_device.h"
-#include "dec_internal.h"
+// Partials, arrival and combine: attn_finish (dec_attn_common.h).
+#include "dec_attn_common.h"
 
 namespace dec {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kChunkMax = 256;  // cache positions per split
-constexpr int kSplitMax = 256;  // splits per kv head
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kCombiners = 8;          // workgroups that combine one kv head's splits
-constexpr unsigned kSpinMax = 1u << 14;  // polls of a waiting combiner before it gives up
-constexpr int kNotCombiner = -1, kGaveUp = -2;   // workgroup roles after arrival (else the combiner slot)
-
-template <int KVT>
-__device__ __forceinline__ void unpack_row(u32x4 v, float* f) {
-  if constexpr (KVT == 1) {
-    f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
-    f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
-  } else {
-    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
-    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
-  }
-}
-
-// Two floats as one agent-scope atomic store (8-byte aligned address).
-__device__ __forceinline__ void store_pair_agent(float* p, float lo, float hi) {
-  const uint64_t v = uint64_t(__float_as_uint(lo)) | (uint64_t(__float_as_uint(hi)) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Two floats with one agent-scope atomic load (8-byte aligned address).
-__device__ __forceinline__ float2 load_pair_agent(const float* p) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
-}
 
 template <int D, int KVT, int G, int NW, bool VLATE>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
@@ -136,6 +90,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   __shared__ float stat[G][2];
   __shared__ float ored[kWaves][G][D];
   __shared__ int role;
+  __shared__ float cwts[kSplitMax][G];
+  __shared__ float cden[G];
+  __shared__ float4 caccs[kBlock];
 
   // ---- scores (log2 units): s_t = (q . k_t) log2(e) / sqrt(d)
   for (int b = 0; b < nsteps; b += U) {
@@ -224,154 +181,45 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       for (int e = 0; e < DPL; ++e) ored[wv][hh][d0 + e] = o[hh][e];
   __syncthreads();
 
-  // ---- this split's partials: o [j][s][G][D] and (m, l) [j][s][G][2], as
-  // agent-scope 64-bit atomic stores (pairs of floats)
-  float* po = a.part + (size_t(j) * a.nsplit + s) * G * D;
-  float* pml = a.part + size_t(a.nkv) * a.nsplit * G * D + (size_t(j) * a.nsplit + s) * G * 2;
-  auto osum = [&](int idx) {
-    const int hh = idx / D, dd = idx % D;
-    float r = ored[0][hh][dd];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) r += ored[w][hh][dd];
-    return r;
-  };
-  for (int i2 = threadIdx.x; i2 < G * D / 2; i2 += kBlock) store_pair_agent(po + 2 * i2, osum(2 * i2), osum(2 * i2 + 1));
-  if (threadIdx.x < G) store_pair_agent(pml + threadIdx.x * 2, stat[threadIdx.x][0], stat[threadIdx.x][1]);
-
-  if (a.partials_only) return;   // the output projection combines them
-
-  // ---- arrival. The last ncomb splits of this kv head to arrive each
-  // combine a slice of its outputs: the earlier ones wait (bounded) until
-  // every split has arrived. Word 0 of the head's counter line counts
-  // arrivals, word 1 finished combiners; the last combiner to finish resets
-  // both for the next launch.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this lane's partial stores have completed
-  __syncthreads();
-  uint32_t* cnt = a.counters + size_t(j) * kCounterStride;
-  // one combiner per ~8 KB of partials (o of every split), at most kCombiners
-  int ncomb = ns * G * D / 2048;
-  ncomb = ncomb < 1 ? 1 : ncomb > kCombiners ? kCombiners : ncomb;
-  if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int slot = int(prev) - (ns - ncomb);   // combiner slot; negative: not a combiner
-    bool gave_up = false;
-    if (slot >= 0 && prev != unsigned(ns - 1)) {
-      unsigned n = 0;
-      // (no_wait, tests of this path: give up without polling)
-      const unsigned spin_max = a.no_wait ? 0u : kSpinMax;
-      while (a.no_wait || __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < unsigned(ns)) {
-        if (++n > spin_max) {   // give up: flag it, write nothing, still count as finished
-          atomicOr(a.err, kErrSync);
-          gave_up = true;
-          break;
-        }
-      }
-    }
-    role = slot < 0 ? kNotCombiner : gave_up ? kGaveUp : slot;
-  }
-  __syncthreads();
-  const int w = role;
-  if (w == kNotCombiner) return;
-
-  if (w >= 0) {
-    // (drop_last, tests of the parity gates: the last split is left out)
-    const int nsum = a.drop_last && ns > 1 ? ns - 1 : ns;
-    const float* pj = a.part + size_t(j) * a.nsplit * G * D;
-    const float* mlj = a.part + size_t(a.nkv) * a.nsplit * G * D + size_t(j) * a.nsplit * G * 2;
-    // this combiner's slice of the float4 outputs; `parts` threads share an
-    // output, each summing every parts-th split, then meet in LDS. The first
-    // kPre splits of each thread are requested before the (m, l) pass, so
-    // both round trips overlap.
-    constexpr int NV = G * D / 4;
-    constexpr int kPre = 8;
-    const int f0 = w * NV / ncomb, f1 = (w + 1) * NV / ncomb;
-    const int len = f1 - f0;
-    const int parts = kBlock / len;
-    const int fi = threadIdx.x % len, part = threadIdx.x / len;
-    const bool active = part < parts;
-    const int f = f0 + fi;
-    float4 pre[kPre];
-#pragma unroll
-    for (int k = 0; k < kPre; ++k) {
-      const int t = part + k * parts;
-      pre[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (active && t < nsum) {
-        const float* pv = pj + size_t(t) * G * D + f * 4;
-        const float2 lo = load_pair_agent(pv), hi = load_pair_agent(pv + 2);
-        pre[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
-      }
-    }
-    // per (split, head): weight exp2(m - M) and the denominator sum of weight * l,
-    // read with agent-scope loads (the partials of other workgroups)
-    __shared__ float wts[kSplitMax][G];
-    __shared__ float den[G];
-    for (int hh = wv; hh < G; hh += kWaves) {
-      float2 ml[kSplitMax / kWave];
-      float M = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < kSplitMax / kWave; ++k) {
-        const int t = lane + k * kWave;
-        ml[k] = t < nsum ? load_pair_agent(mlj + (t * G + hh) * 2) : make_float2(-INFINITY, 0.0f);
-        M = fmaxf(M, ml[k].x);
-      }
-      M = wave_max(M);
-      float dsum = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kSplitMax / kWave; ++k) {
-        const int t = lane + k * kWave;
-        if (t < nsum) {
-          const float wt = exp2f(ml[k].x - M);
-          wts[t][hh] = wt;
-          dsum = fmaf(wt, ml[k].y, dsum);
-        }
-      }
-      dsum = wave_sum(dsum);
-      if (lane == 0) den[hh] = dsum;
-    }
-    __syncthreads();
-    __shared__ float4 accs[kBlock];
-    if (active) {
-      const int hh = (f * 4) / D;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int k = 0; k < kPre; ++k) {
-        const int t = part + k * parts;
-        const float wt = t < nsum ? wts[t][hh] : 0.0f;
-        acc.x = fmaf(pre[k].x, wt, acc.x); acc.y = fmaf(pre[k].y, wt, acc.y);
-        acc.z = fmaf(pre[k].z, wt, acc.z); acc.w = fmaf(pre[k].w, wt, acc.w);
-      }
-      for (int t = part + kPre * parts; t < nsum; t += parts) {
-        const float* pv = pj + size_t(t) * G * D + f * 4;
-        const float2 lo = load_pair_agent(pv), hi = load_pair_agent(pv + 2);
-        const float wt = wts[t][hh];
-        acc.x = fmaf(lo.x, wt, acc.x); acc.y = fmaf(lo.y, wt, acc.y);
-        acc.z = fmaf(hi.x, wt, acc.z); acc.w = fmaf(hi.y, wt, acc.w);
-      }
-      accs[part * len + fi] = acc;
-    }
-    __syncthreads();
-    if (threadIdx.x < len) {
-      const int f = f0 + threadIdx.x;
-      const int hh = (f * 4) / D;
-      float4 acc = accs[threadIdx.x];
-      for (int p = 1; p < parts; ++p) {
-        const float4 v = accs[p * len + threadIdx.x];
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-      }
-      const float r = 1.0f / den[hh];
-      reinterpret_cast<float4*>(a.out + j * G * D)[f] = make_float4(acc.x * r, acc.y * r, acc.z * r, acc.w * r);
-    }
-  }
-  if (threadIdx.x == 0) {
-    if (__hip_atomic_fetch_add(cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == unsigned(ncomb - 1)) {
-      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  attn_finish<D, G, NW>(a, j, s, ns, AttnShared{&ored[0][0][0], &stat[0][0], &cwts[0][0], cden, caccs, &role});
 }
 
 void attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit,
-               int* waves) {
+               int* waves, int* lds) {
+  // The streaming kernel (dec_attn_stream.hip) whenever its chunk's values
+  // fit in LDS: by default about one workgroup per compute unit over the
+  // whole cache (at most 64 splits per kv head), chunks a multiple of 8
+  // positions.
+  const int cmax = attn_lds_max_chunk(n_q, n_kv, head_dim, kvtype);
+  if (chunk_req <= 0 && cmax > 0) {
+    int splits = kLdsTargetGroups / n_kv;
+    splits = splits < 1 ? 1 : splits > 64 ? 64 : splits;
+    int c = (max_ctx + splits - 1) / splits;
+    c = (c + 7) / 8 * 8;
+    if (c > cmax) c = cmax;
+    // only mid-length chunks stream: a stream of a few rows never fills
+    // (the batched kernel's single pass has fewer barriers), and with
+    // 260+ rows per workgroup the batched kernel's three times as many
+    // shorter workgroups balance the compute units better (measured: 7B- and
+    // 9B-shaped 4-bit caches, 34 MB per layer, 8.6 -> 10.2 us and 15.8 ->
+    // 17.4 us streamed)
+    if (c >= kStreamMinRows && c <= kStreamMaxRows && (max_ctx + c - 1) / c <= kSplitMax) {
+      *chunk = c;
+      *nsplit = (max_ctx + c - 1) / c;
+      *waves = kLdsWaves;
+      *lds = 1;
+      return;
+    }
+  }
+  if (chunk_req > 0 && chunk_req <= cmax && (max_ctx + chunk_req - 1) / chunk_req <= kSplitMax) {
+    *chunk = chunk_req;
+    *nsplit = (max_ctx + chunk_req - 1) / chunk_req;
+    *waves = kLdsWaves;
+    *lds = 1;
+    return;
+  }
+  // Otherwise the batched kernel above: rows held in registers in batches
+  // (a requested chunk whose values do not fit in LDS).
   int c = chunk_req;
   int nw = 4;
   if (c <= 0) {
@@ -391,13 +239,6 @@ void attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chu
     // layer at 8320 positions 16.6 -> 16.0 us, 7B-shaped at 2112 positions
     // 12.3 -> 11.95 us)
     if (head_dim == 128 && kvtype == 1 && c > 96) c = 96;
-    // bf16 head_dim 128 with four or more query heads per kv head and up to
-    // 4608 positions (measured on the 9B-shaped layer): 192-row chunks over
-    // 8 waves, one batch per wave and fewer splits to combine
-    if (head_dim == 128 && kvtype == 1 && n_q >= 4 * n_kv && max_ctx <= 4608) {
-      nw = 8;
-      c = 192;
-    }
   }
   const int cmin = (max_ctx + kSplitMax - 1) / kSplitMax;
   if (c < cmin) c = cmin;
@@ -406,6 +247,7 @@ void attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chu
   *chunk = c;
   *nsplit = (max_ctx + c - 1) / c;
   *waves = nw;
+  *lds = 0;
 }
 
 template <int D, int KVT, int NW, bool VL>
@@ -438,6 +280,7 @@ static hipError_t go_attn_waves(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+  if (a.lds) return launch_attn_lds(a, s);
   if (a.nsplit > kSplitMax || a.chunk > kChunkMax) return hipErrorInvalidValue;
   if (a.d == 64) return a.kvtype == 1 ? go_attn_waves<64, 1>(a, s) : go_attn_waves<64, 0>(a, s);
   if (a.d == 128) return a.kvtype == 1 ? go_attn_waves<128, 1>(a, s) : go_attn_waves<128, 0>(a, s);

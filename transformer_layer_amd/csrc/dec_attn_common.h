@@ -1,0 +1,223 @@
+// Split-K decode attention: what every attention kernel shares. The split
+// partials (o unnormalized, and (m, l) with m in log2 units) are stored with
+// agent-scope atomic stores, which reach the device-coherent level by
+// themselves; unless the output projection combines them, the last
+// workgroups of a kv head to arrive (one per ~8 KB of partials, at most
+// kCombiners) combine them with a log-sum-exp rescale, each a slice of the
+// head group's outputs. Every lane waits until its partial stores have
+// completed (vmcnt 0), the workgroup meets at a barrier, and one thread
+// increments the head's arrival counter with an agent-scope atomic.
+// Combiners that arrive before the last one poll that counter (bounded: on
+// giving up they set DEC_ERR_SYNC and write nothing) and read the partials
+// with agent-scope loads. Every counter line is 64 bytes, so the heads'
+// arrivals do not queue on one line; the last combiner to finish resets the
+// line, so a kernel replays unchanged inside a graph.
+#pragma once
+
+#include "dec_device.h"
+#include "dec_internal.h"
+
+namespace dec {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunkMax = 256;  // cache positions per split
+constexpr int kSplitMax = 256;  // splits per kv head
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kCombiners = 8;          // workgroups that combine one kv head's splits
+constexpr unsigned kSpinMax = 1u << 14;  // polls of a waiting combiner before it gives up
+constexpr int kNotCombiner = -1, kGaveUp = -2;   // workgroup roles after arrival (else the combiner slot)
+
+template <int KVT>
+__device__ __forceinline__ void unpack_row(u32x4 v, float* f) {
+  if constexpr (KVT == 1) {
+    f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+    f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+  } else {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+}
+
+// Two floats as one agent-scope atomic store (8-byte aligned address).
+__device__ __forceinline__ void store_pair_agent(float* p, float lo, float hi) {
+  const uint64_t v = uint64_t(__float_as_uint(lo)) | (uint64_t(__float_as_uint(hi)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Two floats with one agent-scope atomic load (8-byte aligned address).
+__device__ __forceinline__ float2 load_pair_agent(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
+}
+
+// LDS the finish step reads or uses: the per-wave output sums
+// ored [NW][G][D], the split's (m, l) stat [G][2], and the combine's
+// scratch: wts [kSplitMax][G], den [G], accs [NW * 64], role.
+struct AttnShared {
+  float* ored;
+  float* stat;
+  float* wts;
+  float* den;
+  float4* accs;
+  int* role;
+};
+
+// Split s of kv head j (of ns live splits): store its partials from LDS,
+// then (unless the output projection combines) arrive and, for the last
+// arrivals, combine. Every thread of the workgroup calls it.
+template <int D, int G, int NW>
+__device__ __forceinline__ void attn_finish(const AttnArgs& a, int j, int s, int ns, AttnShared sh) {
+  // ---- this split's partials: o [j][s][G][D] and (m, l) [j][s][G][2], as
+  // agent-scope 64-bit atomic stores (pairs of floats)
+  constexpr int kWaves = NW;
+  constexpr int kBlock = NW * 64;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  float* po = a.part + (size_t(j) * a.nsplit + s) * G * D;
+  float* pml = a.part + size_t(a.nkv) * a.nsplit * G * D + (size_t(j) * a.nsplit + s) * G * 2;
+  auto osum = [&](int idx) {
+    const int hh = idx / D, dd = idx % D;
+    float r = sh.ored[hh * D + dd];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r += sh.ored[(w * G + hh) * D + dd];
+    return r;
+  };
+  for (int i2 = threadIdx.x; i2 < G * D / 2; i2 += kBlock) store_pair_agent(po + 2 * i2, osum(2 * i2), osum(2 * i2 + 1));
+  if (threadIdx.x < G) store_pair_agent(pml + threadIdx.x * 2, sh.stat[threadIdx.x * 2], sh.stat[threadIdx.x * 2 + 1]);
+
+  if (a.partials_only) return;   // the output projection combines them
+
+  // ---- arrival. The last ncomb splits of this kv head to arrive each
+  // combine a slice of its outputs: the earlier ones wait (bounded) until
+  // every split has arrived. Word 0 of the head's counter line counts
+  // arrivals, word 1 finished combiners; the last combiner to finish resets
+  // both for the next launch.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this lane's partial stores have completed
+  __syncthreads();
+  uint32_t* cnt = a.counters + size_t(j) * kCounterStride;
+  // one combiner per ~8 KB of partials (o of every split), at most kCombiners
+  int ncomb = ns * G * D / 2048;
+  ncomb = ncomb < 1 ? 1 : ncomb > kCombiners ? kCombiners : ncomb;
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int slot = int(prev) - (ns - ncomb);   // combiner slot; negative: not a combiner
+    bool gave_up = false;
+    if (slot >= 0 && prev != unsigned(ns - 1)) {
+      unsigned n = 0;
+      // (no_wait, tests of this path: give up without polling)
+      const unsigned spin_max = a.no_wait ? 0u : kSpinMax;
+      while (a.no_wait || __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < unsigned(ns)) {
+        if (++n > spin_max) {   // give up: flag it, write nothing, still count as finished
+          atomicOr(a.err, kErrSync);
+          gave_up = true;
+          break;
+        }
+      }
+    }
+    *sh.role = slot < 0 ? kNotCombiner : gave_up ? kGaveUp : slot;
+  }
+  __syncthreads();
+  const int w = *sh.role;
+  if (w == kNotCombiner) return;
+
+  if (w >= 0) {
+    // (drop_last, tests of the parity gates: the last split is left out)
+    const int nsum = a.drop_last && ns > 1 ? ns - 1 : ns;
+    const float* pj = a.part + size_t(j) * a.nsplit * G * D;
+    const float* mlj = a.part + size_t(a.nkv) * a.nsplit * G * D + size_t(j) * a.nsplit * G * 2;
+    // this combiner's slice of the float4 outputs; `parts` threads share an
+    // output, each summing every parts-th split, then meet in LDS. The first
+    // kPre splits of each thread are requested before the (m, l) pass, so
+    // both round trips overlap.
+    constexpr int NV = G * D / 4;
+    constexpr int kPre = 8;
+    const int f0 = w * NV / ncomb, f1 = (w + 1) * NV / ncomb;
+    const int len = f1 - f0;
+    const int parts = kBlock / len;
+    const int fi = threadIdx.x % len, part = threadIdx.x / len;
+    const bool active = part < parts;
+    const int f = f0 + fi;
+    float4 pre[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int t = part + k * parts;
+      pre[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (active && t < nsum) {
+        const float* pv = pj + size_t(t) * G * D + f * 4;
+        const float2 lo = load_pair_agent(pv), hi = load_pair_agent(pv + 2);
+        pre[k] = make_float4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+    // per (split, head): weight exp2(m - M) and the denominator sum of weight * l,
+    // read with agent-scope loads (the partials of other workgroups)
+    float* wts = sh.wts;   // [kSplitMax][G]
+    float* den = sh.den;   // [G]
+    for (int hh = wv; hh < G; hh += kWaves) {
+      float2 ml[kSplitMax / kWave];
+      float M = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kSplitMax / kWave; ++k) {
+        const int t = lane + k * kWave;
+        ml[k] = t < nsum ? load_pair_agent(mlj + (t * G + hh) * 2) : make_float2(-INFINITY, 0.0f);
+        M = fmaxf(M, ml[k].x);
+      }
+      M = wave_max(M);
+      float dsum = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kSplitMax / kWave; ++k) {
+        const int t = lane + k * kWave;
+        if (t < nsum) {
+          const float wt = exp2f(ml[k].x - M);
+          wts[t * G + hh] = wt;
+          dsum = fmaf(wt, ml[k].y, dsum);
+        }
+      }
+      dsum = wave_sum(dsum);
+      if (lane == 0) den[hh] = dsum;
+    }
+    __syncthreads();
+    float4* accs = sh.accs;   // [kBlock]
+    if (active) {
+      const int hh = (f * 4) / D;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < kPre; ++k) {
+        const int t = part + k * parts;
+        const float wt = t < nsum ? wts[t * G + hh] : 0.0f;
+        acc.x = fmaf(pre[k].x, wt, acc.x); acc.y = fmaf(pre[k].y, wt, acc.y);
+        acc.z = fmaf(pre[k].z, wt, acc.z); acc.w = fmaf(pre[k].w, wt, acc.w);
+      }
+      for (int t = part + kPre * parts; t < nsum; t += parts) {
+        const float* pv = pj + size_t(t) * G * D + f * 4;
+        const float2 lo = load_pair_agent(pv), hi = load_pair_agent(pv + 2);
+        const float wt = wts[t * G + hh];
+        acc.x = fmaf(lo.x, wt, acc.x); acc.y = fmaf(lo.y, wt, acc.y);
+        acc.z = fmaf(hi.x, wt, acc.z); acc.w = fmaf(hi.y, wt, acc.w);
+      }
+      accs[part * len + fi] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x < len) {
+      const int f = f0 + threadIdx.x;
+      const int hh = (f * 4) / D;
+      float4 acc = accs[threadIdx.x];
+      for (int p = 1; p < parts; ++p) {
+        const float4 v = accs[p * len + threadIdx.x];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      const float r = 1.0f / den[hh];
+      reinterpret_cast<float4*>(a.out + j * G * D)[f] = make_float4(acc.x * r, acc.y * r, acc.z * r, acc.w * r);
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (__hip_atomic_fetch_add(cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == unsigned(ncomb - 1)) {
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+
+}  // namespace dec

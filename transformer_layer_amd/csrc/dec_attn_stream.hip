@@ -1,0 +1,257 @@
+// Split-K decode attention with the keys and the values streaming at once.
+//
+// Grid: n_kv * nsplit workgroups of eight waves, split-major, about one per
+// compute unit. From launch, waves 0-3 stream the chunk's key rows and waves
+// 4-7 its value rows, each lane keeping U 16-byte loads in flight (a ring:
+// each load consumed is replaced at once by the load U rows ahead), so a
+// workgroup has 64 KB in flight for its whole life and the cache streams at
+// the rate a plain streaming kernel reaches. The key waves score each row
+// for every query head of the kv head as it arrives (log2 units, into LDS);
+// the value waves write their rows into LDS. Then one exponential per
+// (head, position) with the chunk's max, the sum of p * v from the LDS
+// values by all eight waves, and the split's partials go to attn_finish
+// (stored, then combined by the last arrivals unless the output projection
+// combines them).
+//
+// The keys are never stored: each is used once, as it arrives. The values
+// wait in LDS for the softmax; only the chunk's values, its scores and the
+// reduction scratch live there.
+//
+// LDS layout (bytes), rows padded to cpad (a whole number of eight-wave
+// row steps): [values cpad x row][scores G x cpad f32][per-wave output sums
+// NW x G x D f32][combine scratch][(m, l) G x 2 f32][role].
+#include "dec_attn_common.h"
+
+namespace dec {
+
+template <int D, int KVT>
+struct StreamShape {
+  static constexpr int EB = KVT == 1 ? 2 : 4;   // bytes per cache element
+  static constexpr int RB = D * EB;             // bytes per cache row
+  static constexpr int DPL = 16 / EB;           // dims per lane (16 bytes)
+  static constexpr int LPR = D / DPL;           // lanes per row
+  static constexpr int RPW = kWave / LPR;       // rows per wave read
+  static constexpr int RPH = RPW * 4;           // rows per step of four waves (keys or values)
+  static constexpr int RPS = RPW * kLdsWaves;   // rows per step of all eight waves
+};
+
+constexpr int kRing = 8;   // loads in flight per lane
+
+__host__ __device__ constexpr int stream_comb_bytes(int G) {
+  return ((kSplitMax * G + G) * 4 + 15) / 16 * 16 + kLdsWaves * 64 * 16;
+}
+__host__ __device__ constexpr int stream_lds_bytes(int cpad, int rb, int G, int D) {
+  return cpad * rb + G * cpad * 4 + kLdsWaves * G * D * 4 + stream_comb_bytes(G) + G * 2 * 4 + 16;
+}
+
+template <int D, int KVT, int G>
+__global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a) {
+  using S = StreamShape<D, KVT>;
+  constexpr int NW = kLdsWaves;
+  constexpr int RB = S::RB, DPL = S::DPL, LPR = S::LPR, RPW = S::RPW, RPH = S::RPH, RPS = S::RPS;
+  constexpr int U = kRing;
+  static_assert(LPR >= 2 && LPR <= 32, "row layout");
+  extern __shared__ __align__(16) uint8_t smem[];
+
+  if (a.null_kernel) return;
+  const int j = blockIdx.x % a.nkv;
+  const int s = blockIdx.x / a.nkv;
+  const int pos = *a.pos;
+  if (pos < 0 || pos >= a.max_ctx) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.err, kErrPos);
+    return;
+  }
+  const int L = pos + 1;
+  const int ns = (L + a.chunk - 1) / a.chunk;
+  if (s >= ns) return;
+  const int t0 = s * a.chunk;
+  const int n = min(t0 + a.chunk, L) - t0;
+  const int cpad = (a.chunk + RPS - 1) / RPS * RPS;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int sub = lane / LPR;
+  const int li = lane % LPR;
+  const int d0 = li * DPL;
+
+  uint8_t* vbuf = smem;                                                   // [cpad][RB]
+  float* sc = reinterpret_cast<float*>(smem + cpad * RB);                 // [G][cpad]
+  float* ored = sc + G * cpad;                                            // [NW][G][D]
+  float* wts = ored + NW * G * D;                                         // [kSplitMax][G]
+  float* den = wts + kSplitMax * G;                                       // [G]
+  uint8_t* after = reinterpret_cast<uint8_t*>(ored + NW * G * D) + stream_comb_bytes(G) - NW * 64 * 16;
+  float4* accs = reinterpret_cast<float4*>(after);                        // [NW * 64]
+  float* stat = reinterpret_cast<float*>(after + NW * 64 * 16);           // [G][2]
+  int* role = reinterpret_cast<int*>(stat + G * 2);
+
+  // waves 0-3 stream keys, waves 4-7 values: row r of the chunk is read by
+  // wave (r / RPW) % 4 of its half at step r / RPH
+  const bool keys = wv < 4;
+  const int hw = keys ? wv : wv - 4;
+  const int nsteps = (n + RPH - 1) / RPH;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(keys ? a.kc : a.vc) +
+                       (size_t(j) * a.max_ctx + t0) * RB + li * 16;
+  auto row_of = [&](int step) { return step * RPH + hw * RPW + sub; };
+  auto load = [&](int step) {
+    int r = row_of(step);
+    r = r < n ? r : n - 1;   // every load is issued: past the chunk, its last row again
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + size_t(r) * RB));
+  };
+  // the ring: slot u holds step k0 + u; a consumed slot is refilled at once
+  // with the step U ahead. Every load is issued (a step past the chunk
+  // re-reads its last row, a cache hit): refilled conditionally, the
+  // compiler waited for the whole ring before each use.
+  u32x4 ring[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) ring[u] = load(u);
+
+  if (keys) {
+    const float qscale = kLog2e / sqrtf(float(D));
+    float qv[G][DPL];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < DPL; e += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(a.q + (j * G + hh) * D + d0 + e);
+        qv[hh][e] = x.x * qscale; qv[hh][e + 1] = x.y * qscale;
+        qv[hh][e + 2] = x.z * qscale; qv[hh][e + 3] = x.w * qscale;
+      }
+    // ---- scores (log2 units): s_t = (q . k_t) log2(e) / sqrt(d)
+    for (int k0 = 0; k0 < nsteps; k0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const u32x4 w = ring[u];
+        ring[u] = load(k0 + U + u);
+        if (k0 + u < nsteps) {
+          const int t = row_of(k0 + u);
+          float kf[DPL];
+          unpack_row<KVT>(w, kf);
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            float p = 0.0f;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) p = fmaf(qv[hh][e], kf[e], p);
+            p = group_sum<LPR>(p);
+            if (t < n && li == 0) sc[hh * cpad + t] = p;
+          }
+        }
+      }
+    }
+  } else {
+    // ---- values into LDS as they arrive
+    for (int k0 = 0; k0 < nsteps; k0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const u32x4 w = ring[u];
+        ring[u] = load(k0 + U + u);
+        if (k0 + u < nsteps) {
+          const int t = row_of(k0 + u);   // < cpad: the steps cover at most cpad rows
+          *reinterpret_cast<u32x4*>(vbuf + t * RB + li * 16) = w;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- per head: m = max s, p = exp2(s - m), l = sum p
+  for (int hh = wv; hh < G; hh += NW) {
+    float m = -INFINITY;
+    for (int i = lane; i < n; i += kWave) m = fmaxf(m, sc[hh * cpad + i]);
+    m = wave_max(m);
+    float l = 0.0f;
+    for (int i = lane; i < n; i += kWave) {
+      const float p = exp2f(sc[hh * cpad + i] - m);
+      sc[hh * cpad + i] = p;
+      l += p;
+    }
+    l = wave_sum(l);
+    if (lane == 0) { stat[hh * 2] = m; stat[hh * 2 + 1] = l; }
+  }
+  __syncthreads();
+
+  // ---- o = sum_t p_t v_t, all eight waves over the LDS values
+  float o[G][DPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[hh][e] = 0.0f;
+  const int nsteps8 = (n + RPS - 1) / RPS;
+  for (int b = 0; b < nsteps8; ++b) {
+    const int t = b * RPS + wv * RPW + sub;
+    if (t < n) {
+      float vf[DPL];
+      unpack_row<KVT>(*reinterpret_cast<const u32x4*>(vbuf + t * RB + li * 16), vf);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float p = sc[hh * cpad + t];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[hh][e] = fmaf(p, vf[e], o[hh][e]);
+      }
+    }
+  }
+  // rows of one wave read sit LPR lanes apart: fold them
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[hh][e] = fold_groups<LPR>(o[hh][e]);
+  if (sub == 0)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ored[(wv * G + hh) * D + d0 + e] = o[hh][e];
+  __syncthreads();
+
+  attn_finish<D, G, NW>(a, j, s, ns, AttnShared{ored, stat, wts, den, accs, role});
+}
+
+// rows per eight-wave step and bytes per row of a shape
+static void stream_row_shape(int head_dim, int kvtype, int* rps, int* rb) {
+  const int eb = kvtype == 1 ? 2 : 4;
+  *rb = head_dim * eb;
+  const int lpr = head_dim * eb / 16;
+  *rps = (kWave / lpr) * kLdsWaves;
+}
+
+static bool stream_fits(int n_q, int n_kv, int head_dim, int kvtype, int chunk) {
+  int rps, rb;
+  stream_row_shape(head_dim, kvtype, &rps, &rb);
+  const int cpad = (chunk + rps - 1) / rps * rps;
+  return stream_lds_bytes(cpad, rb, n_q / n_kv, head_dim) <= kLdsBudget;
+}
+
+int attn_lds_max_chunk(int n_q, int n_kv, int head_dim, int kvtype) {
+  int rps, rb;
+  stream_row_shape(head_dim, kvtype, &rps, &rb);
+  if (!stream_fits(n_q, n_kv, head_dim, kvtype, rps)) return 0;
+  int c = rps;
+  while (stream_fits(n_q, n_kv, head_dim, kvtype, c + rps)) c += rps;
+  return c;
+}
+
+template <int D, int KVT>
+static hipError_t go_attn_stream(const AttnArgs& a, hipStream_t s) {
+  using S = StreamShape<D, KVT>;
+  const int g = a.nq / a.nkv;
+  const int cpad = (a.chunk + S::RPS - 1) / S::RPS * S::RPS;
+  const int lds = stream_lds_bytes(cpad, S::RB, g, D);
+  if (lds > kLdsBudget) return hipErrorInvalidValue;
+  const dim3 grid(a.nkv * a.nsplit), block(kLdsWaves * 64);
+  switch (g) {
+    case 1: hipLaunchKernelGGL((attn_stream_kernel<D, KVT, 1>), grid, block, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_stream_kernel<D, KVT, 2>), grid, block, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_stream_kernel<D, KVT, 4>), grid, block, lds, s, a); break;
+    case 8: hipLaunchKernelGGL((attn_stream_kernel<D, KVT, 8>), grid, block, lds, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_lds(const AttnArgs& a, hipStream_t s) {
+  if (a.nsplit > kSplitMax) return hipErrorInvalidValue;
+  if (a.d == 64) return a.kvtype == 1 ? go_attn_stream<64, 1>(a, s) : go_attn_stream<64, 0>(a, s);
+  if (a.d == 128) return a.kvtype == 1 ? go_attn_stream<128, 1>(a, s) : go_attn_stream<128, 0>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dec

@@ -97,16 +97,30 @@ struct AttnArgs {
   uint32_t* err;
   int nq, nkv, d, max_ctx, chunk, nsplit, kvtype;
   int waves;           // waves per workgroup (4 or 8)
+  int lds;             // 1: the streaming kernel (dec_attn_stream.hip), values staged in LDS
   int no_wait;         // combiners give up at once when splits are missing (failure-path tests)
   int partials_only;   // write the splits' partials and stop (the output projection combines them)
   int drop_last;       // test-only fault: the combine leaves out the last split (two or more splits)
   int null_kernel;
 };
 
-// attention chunk (positions per split), split count and waves per workgroup for a shape
+// attention chunk (positions per split), split count, waves per workgroup
+// and kernel (lds = 1: the streaming kernel) for a shape
 void attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit,
-               int* waves);
+               int* waves, int* lds);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+// The streaming attention kernel: eight waves per workgroup; the longest
+// chunk (a multiple of its row step) whose values, scores and scratch fit in
+// one workgroup's LDS (0 if none does); planned for about kLdsTargetGroups
+// workgroups (one per compute unit of an MI355X).
+constexpr int kLdsWaves = 8;
+constexpr int kLdsTargetGroups = 256;
+constexpr int kStreamMinRows = 64;    // default chunks outside [min, max] rows
+constexpr int kStreamMaxRows = 160;   // take the batched kernel
+constexpr int kLdsBudget = 163840;   // LDS one workgroup may use on gfx950
+int attn_lds_max_chunk(int n_q, int n_kv, int head_dim, int kvtype);
+hipError_t launch_attn_lds(const AttnArgs& a, hipStream_t s);
 
 // Attention combine fused into the output projection (bf16): x += Wo a, a
 // combined from the partials of at most kAttnOSplits splits per kv head.
