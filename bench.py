@@ -231,6 +231,137 @@ def cpu_baseline(cfg, budget_s: float = 15.0):
             "host_cores_available": cores, "blas_threads": blas_threads}
 
 
+def timed_token_bytes(cfg, steps: int) -> float:
+    """Algorithmic bytes per token over the positions a timed run of `steps`
+    graph replays visits: ctx, ctx + 1, ..., wrapping to ctx after the
+    decode window as the position advance does. Weights and norms of every
+    layer, the KV read over 0..p and the KV write (synth.token_bytes's
+    terms), the read averaged over the positions actually timed."""
+    import synth
+    mean_len = sum(cfg.ctx + (i % cfg.steps) + 1 for i in range(steps)) / steps
+    kv = synth.kv_bytes(cfg, 1)
+    wb = sum(synth.layer_weight_bytes(cfg).values())
+    return cfg.n_layers * (wb + kv["read"] * mean_len + kv["write"])
+
+
+def gpu_clocks() -> dict:
+    """Current GPU clocks as rocm-smi reports them (best effort)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=15).stdout
+    except Exception as e:  # pragma: no cover
+        return {"error": str(e)}
+    clk = {}
+    for line in out.splitlines():
+        low = line.lower()
+        for key in ("sclk", "mclk", "fclk", "socclk"):
+            if f"{key} clock level" in low and "(" in line:
+                clk[key] = line.split("(")[-1].split(")")[0]
+    return clk or {"raw": out[-400:]}
+
+
+class Workload:
+    """One stack on the GPU with its per-token graph, ready to time."""
+
+    def __init__(self, cfg, flags=0, chunk=0, eager=False):
+        import synth
+        self.cfg = cfg
+        self.st = build_stack(cfg, flags, chunk)
+        self.toks = synth.tokens(cfg, cfg.steps)
+        self.st.set_token_list(self.toks)
+        self.lo, self.hi = cfg.ctx, cfg.ctx + cfg.steps
+        self.reset()
+        if eager:
+            self.step = lambda: self.st.token_step(self.lo, self.hi)  # noqa: E731
+        else:
+            self.graph = self.st.capture(self.lo, self.hi)
+            self.reset()
+            self.step = self.graph.replay
+
+    def reset(self):
+        self.st.set_pos(self.lo)
+        self.st.set_token(int(self.toks[0]))
+
+    def timed(self, steps: int, warmup: int):
+        """Warm up, reset the position, then time exactly `steps` tokens with
+        HIP events on the current stream. Returns (ms, wall seconds)."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        self.reset()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t_wall = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            self.step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), time.perf_counter() - t_wall
+
+    def close(self):
+        import torch
+        self.graph = None
+        self.step = None
+        self.st = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def other_workload(name: str, steps: int, warmup: int, repeats: int) -> dict:
+    """tok/s of another workload's stack: the median of `repeats` timed runs
+    of `steps` tokens (same protocol as the headline)."""
+    import synth
+    cfg = synth.CONFIGS[name]
+    log(f"config {cfg.name}: building stack ({cfg.n_layers} layers)")
+    w = Workload(cfg)
+    runs = []
+    for r in range(repeats):
+        ms, _ = w.timed(steps, warmup if r == 0 else 2)
+        runs.append(steps / (ms * 1e-3))
+    err = w.st.check_err()
+    w.close()
+    tok_s = float(np.median(runs))
+    bpt = timed_token_bytes(cfg, steps)
+    gbs = bpt * tok_s / 1e9
+    out = {"tok_s": round(tok_s, 2), "tok_s_runs": [round(v, 2) for v in runs], "ms_per_step": round(1e3 / tok_s, 4),
+           "bytes_per_token": int(bpt), "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+           "layers": cfg.n_layers, "weights": cfg.wtype, "context": cfg.ctx, "device_error": err}
+    if name in ("C3", "C4", "C5"):
+        out["target_70pct_tok_s"] = round(0.7 * PEAK_HBM_GBS * 1e9 / bpt, 1)
+    log(f"{cfg.name}: {tok_s:.1f} tok/s, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.3f} of peak)")
+    return out
+
+
+def ab_modes(cfg, steps: int, warmup: int) -> dict:
+    """The pages' levers on the current kernels, each on the same workload and
+    timing: graph replay vs per-token host launches, the fused five-kernel
+    layer vs the ten per-op kernels, and the null-kernel graph (every launch
+    kept, every body empty: the boundary cost per token)."""
+    from transformer_layer_amd import lib as L
+    modes = [("fused-graph", 0, False), ("fused-eager", 0, True), ("unfused-graph", L.DEC_UNFUSED, False),
+             ("null-kernels-graph", L.DEC_NULL_KERNELS, False), ("null-kernels-unfused-graph",
+                                                                  L.DEC_NULL_KERNELS | L.DEC_UNFUSED, False)]
+    out = {}
+    for name, flags, eager in modes:
+        w = Workload(cfg, flags=flags, eager=eager)
+        runs = [w.timed(steps, warmup if r == 0 else 2)[0] / steps for r in range(3)]
+        w.close()
+        ms = float(np.median(runs))
+        out[name] = {"ms_per_token": round(ms, 4), "tok_s": round(1e3 / ms, 2),
+                     "runs_ms": [round(v, 4) for v in runs]}
+        log(f"{name}: {ms:.4f} ms/token")
+    nl = cfg.n_layers
+    per_tok = {"fused": 2 + 5 * nl, "unfused": 2 + 10 * nl}
+    out["dispatches_per_token"] = per_tok
+    out["boundary_us"] = round(out["null-kernels-graph"]["ms_per_token"] * 1e3 / per_tok["fused"], 3)
+    out["fusion_speedup"] = round(out["unfused-graph"]["ms_per_token"] / out["fused-graph"]["ms_per_token"], 4)
+    out["graph_speedup"] = round(out["fused-eager"]["ms_per_token"] / out["fused-graph"]["ms_per_token"], 4)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +374,12 @@ def main() -> int:
     ap.add_argument("--attn-chunk", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip the greedy (LM head) timing")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed runs of --steps tokens for the median (the first is the headline value)")
+    ap.add_argument("--others", default="C3,C5,C2",
+                    help="other workloads timed the same way and reported under `workloads` ('' for none)")
+    ap.add_argument("--ab", action="store_true",
+                    help="only the paired A/B modes (graph/eager, fused/unfused, null kernels) on --config")
     ap.add_argument("--ffn-reps", type=int, default=4,
                     help="back-to-back sweeps over the layers when timing the gated-FFN kernel")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -258,49 +395,29 @@ def main() -> int:
     from transformer_layer_amd import lib as L
 
     cfg = synth.CONFIGS[args.config]
+    if args.ab:
+        res = ab_modes(cfg, args.steps, args.warmup)
+        print(json.dumps({"config": cfg.name, "steps": args.steps, "ab": res}), flush=True)
+        return 0
     flags = (L.DEC_UNFUSED if args.unfused else 0) | (L.DEC_NULL_KERNELS if args.null_kernels else 0)
     log(f"config {cfg.name}: building stack ({cfg.n_layers} layers)")
-    st = build_stack(cfg, flags, args.attn_chunk)
-    toks = synth.tokens(cfg, cfg.steps)
-    st.set_token_list(toks)
-    lo, hi = cfg.ctx, cfg.ctx + cfg.steps
-
-    def reset():
-        st.set_pos(lo)
-        st.set_token(int(toks[0]))
-
-    reset()
-    stream = torch.cuda.current_stream()
-    if args.eager:
-        step = lambda: st.token_step(lo, hi)  # noqa: E731
-    else:
-        g = st.capture(lo, hi)
-        reset()
-        step = g.replay
-    log("warmup")
-    for _ in range(args.warmup):
-        step()
-    reset()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    w = Workload(cfg, flags, args.attn_chunk, eager=args.eager)
+    st = w.st
     log(f"timing {args.steps} steps")
-    t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1)
+    ms, wall = w.timed(args.steps, args.warmup)
     err = st.check_err()
     if err:
         log(f"device error word {err:#x}")
         return 1
     tok_s = args.steps / (ms * 1e-3)
-    bpt = synth.token_bytes(cfg)
+    bpt = timed_token_bytes(cfg, args.steps)
     gbs = bpt * tok_s / 1e9
     log(f"{tok_s:.1f} tok/s, {ms / args.steps:.3f} ms/token, {gbs:.0f} GB/s")
+    reps = [tok_s]
+    for _ in range(max(0, args.repeats - 1)):
+        reps.append(args.steps / (w.timed(args.steps, 2)[0] * 1e-3))
+    log(f"repeat runs: {', '.join(f'{v:.1f}' for v in reps)} tok/s")
+    lo, hi = w.lo, w.hi
 
     head = None
     if not args.null_kernels and not args.no_head:
@@ -308,7 +425,7 @@ def main() -> int:
 
     roof = None
     if not args.null_kernels:
-        reset()
+        w.reset()
         t_ffn, n_ffn, t_ffn_host = ffn_kernel_time(st, cfg, args.ffn_reps)
         ffn_bytes = synth.layer_weight_bytes(cfg)["ffn"]
         ach = ffn_bytes / t_ffn / 1e9
@@ -319,9 +436,16 @@ def main() -> int:
                 "avg_launch_us": round(t_ffn * 1e6, 2), "timing": "graph-replayed sweep, HIP events",
                 "host_launched_avg_us": round(t_ffn_host * 1e6, 2)}
         log(f"gated FFN: {t_ffn * 1e6:.1f} us/launch, {ach:.0f} GB/s")
+    w.close()
+    del st
 
     if args.calib_copy:
         calib_copy(args.calib_copy)
+
+    others = {}
+    if not args.null_kernels and not args.unfused and not args.eager:
+        for name in [n for n in args.others.split(",") if n and n != args.config]:
+            others[synth.CONFIGS[name].name] = other_workload(name, args.steps, args.warmup, 3)
 
     cpu = None
     if not args.no_cpu:
@@ -352,10 +476,14 @@ def main() -> int:
         "bytes_per_token": int(bpt),
         "hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "target_70pct_tok_s": round(0.7 * PEAK_HBM_GBS * 1e9 / bpt, 1),
+        "repeat_runs": {"tok_s": [round(v, 2) for v in reps], "median": round(float(np.median(reps)), 2)},
         "wall_s_timed": round(wall, 3),
+        "gpu_clocks": gpu_clocks(),
         "roofline": roof,
         "cpu_baseline": cpu,
         "with_head": head,
+        "workloads": others,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -99,16 +99,17 @@ def head_bytes(c: DecodeConfig) -> float:
     return c.vocab * c.hidden * elem_bytes(c.htype) + c.hidden * elem_bytes(c.ntype)
 
 
-def token_bytes(c: DecodeConfig) -> float:
+def token_bytes(c: DecodeConfig, steps: int = None) -> float:
     """Algorithmic HBM bytes of one decode token of the layer stack.
 
     Weights and norms of every layer, plus the KV read averaged over the
-    decode window (the cache holds ctx+1 .. ctx+steps entries while the
-    window runs), plus the KV write. Activations (tens of KB) and the LM head
-    are not counted.
+    first `steps` decode positions (default: the whole decode window; the
+    cache holds ctx+1 .. ctx+steps entries while they run), plus the KV
+    write. Activations (tens of KB) and the LM head are not counted.
     """
+    n = c.steps if steps is None else steps
     wb = sum(layer_weight_bytes(c).values())
-    avg_len = c.ctx + (c.steps + 1) / 2.0
+    avg_len = c.ctx + (n + 1) / 2.0
     kv = kv_bytes(c, 1)
     per_layer = wb + kv["read"] * avg_len + kv["write"]
     return per_layer * c.n_layers

@@ -72,3 +72,22 @@ def test_head_bytes_by_hand(name, hbytes, nbytes):
     4-bit workload) and the final norm weight."""
     c = synth.CONFIGS[name]
     assert synth.head_bytes(c) == c.vocab * c.hidden * hbytes + c.hidden * nbytes
+
+
+@pytest.mark.parametrize("name", ["C2", "C3", "C4", "C5"])
+def test_timed_bytes_follow_the_positions_timed(name):
+    """The bench's bytes per token average the KV read over the positions
+    its timed run visits: the whole window equals token_bytes, 20 steps the
+    first 20 positions, and a run longer than the window wraps to ctx."""
+    c = synth.CONFIGS[name]
+    assert bench.timed_token_bytes(c, c.steps) == pytest.approx(synth.token_bytes(c), rel=1e-12)
+    assert bench.timed_token_bytes(c, 20) == pytest.approx(synth.token_bytes(c, 20), rel=1e-12)
+    want20 = _by_hand(c.hidden, c.n_q_heads, c.n_kv_heads, c.head_dim, c.ffn, c.n_layers, c.ctx, 20,
+                      synth.elem_bytes(c.wtype), 2, 2)
+    assert bench.timed_token_bytes(c, 20) == pytest.approx(want20, rel=1e-12)
+    # two windows and 3 more steps: the mean over ctx+1..ctx+steps twice, then ctx+1..ctx+3
+    n = 2 * c.steps + 3
+    lens = [c.ctx + (i % c.steps) + 1 for i in range(n)]
+    per_pos = 2 * c.n_kv_heads * c.head_dim * 2
+    want = synth.token_bytes(c) + c.n_layers * per_pos * (sum(lens) / n - (c.ctx + (c.steps + 1) / 2))
+    assert bench.timed_token_bytes(c, n) == pytest.approx(want, rel=1e-12)
