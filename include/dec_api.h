@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define DEC_ABI_VERSION 3
+#define DEC_ABI_VERSION 4
 
 enum dec_dtype { DEC_F32 = 0, DEC_BF16 = 1, DEC_Q4 = 2 };
 
@@ -97,6 +97,20 @@ enum dec_status {
                                     projection is a plain dec_gemv_residual */
 #define DEC_DETERMINISTIC 0x20u /* no float atomics on the path, so repeated runs give the
                                    same bits (takes the DEC_NO_FUSE_ATTN_O path) */
+
+/* Which attention kernel runs (a two-bit field; 0 = the library's choice
+   for the shape). All three compute the same split-K reduction ("RDNA4
+   Decode Kernel Fusion...", section "Where fusion stops"); they differ in
+   how a workgroup's rows reach the softmax. A kernel that cannot run the
+   shape or attn_chunk makes every entry point return DEC_E_SHAPE. */
+#define DEC_ATTN_KERNEL_MASK 0x3000u
+#define DEC_ATTN_BATCHED 0x1000u /* rows in registers in batches, one softmax per workgroup
+                                    through LDS (any cache type; chunks up to 256) */
+#define DEC_ATTN_STREAM 0x2000u  /* keys scored as they arrive, values staged in LDS
+                                    (chunks whose values fit in LDS) */
+#define DEC_ATTN_LOCAL 0x3000u   /* every row requested at launch, a softmax per wave,
+                                    waves rescaled once (bf16 cache; chunks up to 9 row
+                                    steps of eight waves: 288 positions at d = 128) */
 /* Tests only. DEC_TEST_NO_WAIT exercises a failure path: an attention
    combiner that finds splits of its kv head still missing gives up at once
    (DEC_ERR_SYNC, its output slice not written) instead of polling. The

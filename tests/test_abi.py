@@ -202,6 +202,30 @@ def test_bad_descriptor_is_rejected(L, field, value, code, word):
     assert L.load().dec_attn_part_floats(ctypes.byref(d)) == -1
 
 
+@pytest.mark.parametrize("kernel,over", [
+    ("DEC_ATTN_LOCAL", {"kvtype": 0}),                        # the wave-local kernel reads bf16 caches only
+    ("DEC_ATTN_STREAM", {"kvtype": 0, "n_q_heads": 64, "attn_chunk": 256}),  # f32 values beyond LDS
+    ("DEC_ATTN_BATCHED", {"max_ctx": 100000}),                # 391 splits of at most 256 positions
+])
+def test_attention_kernel_that_cannot_run_the_shape_is_refused(L, kernel, over):
+    d = desc_of(L, synth.CONFIGS["C4"], flags=getattr(L, kernel), **over)
+    assert rc_step(L, d, weights_of(L), state_of(L)) == E_SHAPE
+    assert L.load().dec_attn_part_floats(ctypes.byref(d)) == -1
+
+
+@pytest.mark.parametrize("name", ["C2", "C3", "C4", "C5"])
+def test_every_attention_kernel_plans_the_workloads(L, name):
+    """Each kernel, forced, plans every bf16-cache workload (C2-C5) within
+    256 splits, and the library default's partials fit one of them."""
+    cfg = synth.CONFIGS[name]
+    sizes = []
+    for k in ("DEC_ATTN_BATCHED", "DEC_ATTN_STREAM", "DEC_ATTN_LOCAL"):
+        n = L.dec_attn_part_floats(desc_of(L, cfg, flags=getattr(L, k)))
+        assert n > 0, (name, k, L.dec_last_error())
+        sizes.append(n)
+    assert L.dec_attn_part_floats(desc_of(L, cfg)) in sizes
+
+
 def test_null_arguments_are_rejected(L):
     lib = L.load()
     cfg = synth.CONFIGS["C4"]

@@ -107,6 +107,20 @@ def test_deterministic_flag_repeats_bit_for_bit(gpu, cfg_name):
     assert _worst(a, _oracle_run(cfg)) <= TOL
 
 
+@pytest.mark.parametrize("kernel", ["DEC_ATTN_BATCHED", "DEC_ATTN_STREAM", "DEC_ATTN_LOCAL"])
+@pytest.mark.parametrize("combine", ["in the output projection", "in the attention kernel"])
+def test_layer_step_with_each_attention_kernel(gpu, kernel, combine):
+    """The bf16 layer step with each attention kernel forced, its partials
+    combined in the output projection or by the attention's own combiners:
+    every layer of every step against the oracle (cache from position 0, so
+    the splits grow from one to three)."""
+    cfg = _bf16_cfg(steps=24)
+    flags = getattr(L, kernel) | (L.DEC_NO_FUSE_ATTN_O if combine == "in the attention kernel" else 0)
+    got, _, _, err = _run(cfg, flags=flags, attn_chunk=10)
+    assert err == 0
+    assert _worst(got, _oracle_run(cfg)) <= TOL
+
+
 def test_split_attention_entry_points_match_oracle(gpu):
     """dec_attn_partials then dec_attn_o_residual on a layer whose cache holds
     several splits of positions: x becomes x + Wo attention(q)."""

@@ -196,6 +196,44 @@ def test_attn_splitk(gpu, d, kvtype, nq, nkv, max_ctx, positions, chunk):
     assert st.check_err() == 0
 
 
+KERNEL_CASES = [
+    # d, n_q, n_kv, max_ctx, positions, chunk (bf16 cache: every kernel runs it)
+    (64, 32, 8, 640, (0, 511, 639), 0),
+    (128, 32, 32, 2176, (2047,), 0),
+    (128, 16, 2, 300, (0, 1, 16, 17, 299), 16),   # one-row and ragged splits
+    (128, 8, 4, 700, (699, 350), 100),            # chunks that end inside a row step
+    (64, 8, 8, 1000, (999, 0), 200),
+    (128, 32, 8, 4352, (4351,), 0),
+]
+
+
+@pytest.mark.parametrize("kernel", ["DEC_ATTN_BATCHED", "DEC_ATTN_STREAM", "DEC_ATTN_LOCAL"])
+@pytest.mark.parametrize("d,nq,nkv,max_ctx,positions,chunk", KERNEL_CASES)
+def test_attn_each_kernel(gpu, kernel, d, nq, nkv, max_ctx, positions, chunk):
+    """Every attention kernel, forced by its flag, on the same shapes: the
+    same split-K result as the oracle, the counters reset, no error."""
+    cfg = synth.tiny(hidden=256, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, ffn=256, wtype="bf16",
+                     ntype="bf16", kvtype="bf16", ctx=0, steps=max_ctx, seed=9)
+    st = DecodeStack(cfg, n_layers=1, attn_chunk=chunk, flags=getattr(L, kernel))
+    std = 0.02 * np.sqrt(4096)
+    K = synth.rand_cache((9, 1, max_ctx), nkv, max_ctx, d, "bf16", std)
+    V = synth.rand_cache((9, 2, max_ctx), nkv, max_ctx, d, "bf16", std)
+    st.set_prefill(0, K, V)
+    Kv = oracle.ref.cache_values(K.data, "bf16", np.float64)
+    Vv = oracle.ref.cache_values(V.data, "bf16", np.float64)
+    for i, p in enumerate(positions):
+        q = synth.rand_f32((9, 3, i), (nq, d), std=std)
+        st.q.copy_(torch.from_numpy(q.reshape(-1)))
+        st.set_pos(p)
+        st.attn.fill_(float("nan"))
+        L.dec_attn_splitk(st.desc, st.state[0])
+        torch.cuda.synchronize()
+        ref = oracle.attend(q.astype(np.float64), Kv[:, : p + 1], Vv[:, : p + 1], nq // nkv)
+        assert rel_l2(st.attn.cpu().numpy(), ref.reshape(-1)) <= TOL, f"{kernel} pos {p}"
+        assert int(st.counters.abs().sum().item()) == 0, "arrival counters not reset"
+    assert st.check_err() == 0
+
+
 def test_combiner_give_up_sets_sync_error_and_recovers(gpu):
     """The attention combine's failure path, forced from the host:
     DEC_TEST_NO_WAIT makes every combiner but the last arrival of a kv head

@@ -33,6 +33,22 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int ge_of(int wtype) { return wtype == DEC_F32 ? 4 : wtype == DEC_BF16 ? 8 : 32; }
 
+// The attention plan of a layer shape: the kernel DEC_ATTN_* in its flags
+// asks for (the library's choice without one) and its chunk, split count
+// and waves. Every entry point plans through here, so the partials' layout,
+// the kernel and the output projection's combine always agree.
+bool attn_plan_of(const dec_layer_desc* d, int* chunk, int* ns, int* nw, int* kind) {
+  int req = dec::kAttnDefault;
+  switch (d->flags & DEC_ATTN_KERNEL_MASK) {
+    case DEC_ATTN_BATCHED: req = dec::kAttnBatched; break;
+    case DEC_ATTN_STREAM: req = dec::kAttnStream; break;
+    case DEC_ATTN_LOCAL: req = dec::kAttnLocal; break;
+    default: break;
+  }
+  return dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx,
+                        d->attn_chunk, req, chunk, ns, nw, kind);
+}
+
 int check_desc(const dec_layer_desc* d) {
   if (!d) return fail(DEC_E_NULL, "desc is NULL");
   if (d->wtype < DEC_F32 || d->wtype > DEC_Q4) return fail(DEC_E_DTYPE, "wtype %d", d->wtype);
@@ -50,10 +66,11 @@ int check_desc(const dec_layer_desc* d) {
   if (d->max_ctx <= 0 || d->max_ctx > (1 << 20)) return fail(DEC_E_SHAPE, "max_ctx %d", d->max_ctx);
   if (!(d->rms_eps >= 0.0f)) return fail(DEC_E_SHAPE, "rms_eps");
   if (d->attn_chunk < 0 || d->attn_chunk > 256) return fail(DEC_E_SHAPE, "attn_chunk %d (0..256)", d->attn_chunk);
-  int chunk, ns, nw, lds;
-  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
-                 &chunk, &ns, &nw, &lds);
-  if (ns > 256) return fail(DEC_E_SHAPE, "max_ctx %d needs %d splits (max 256)", d->max_ctx, ns);
+  int chunk, ns, nw, kind;
+  if (!attn_plan_of(d, &chunk, &ns, &nw, &kind)) {
+    if (ns > 256) return fail(DEC_E_SHAPE, "max_ctx %d needs %d splits (max 256)", d->max_ctx, ns);
+    return fail(DEC_E_SHAPE, "attention kernel %d cannot run chunk %d of this shape", kind, chunk);
+  }
   return DEC_OK;
 }
 
@@ -127,8 +144,7 @@ int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t 
   a.no_wait = (d->flags & DEC_TEST_NO_WAIT) ? 1 : 0;
   a.drop_last = (d->flags & DEC_TEST_DROP_SPLIT) ? 1 : 0;
   a.partials_only = partials_only ? 1 : 0;
-  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
-                 &a.chunk, &a.nsplit, &a.waves, &a.lds);
+  attn_plan_of(d, &a.chunk, &a.nsplit, &a.waves, &a.kind);
   return launched(dec::launch_attn(a, s), "attn_splitk");
 }
 
@@ -136,8 +152,8 @@ int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t 
 // split count it supports.
 bool attn_o_possible(const dec_layer_desc* d) {
   if (d->wtype != DEC_BF16 || d->kvtype != DEC_BF16) return false;
-  int chunk, ns, nw, lds;
-  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, 1, d->max_ctx, d->attn_chunk, &chunk, &ns, &nw, &lds);
+  int chunk, ns, nw, kind;
+  attn_plan_of(d, &chunk, &ns, &nw, &kind);
   return dec::attn_o_supported(d->n_q_heads, d->n_kv_heads, d->head_dim, ns);
 }
 
@@ -163,9 +179,8 @@ int attn_o_launch(const dec_layer_desc* d, dec_mat wo, const dec_layer_state* st
   a.max_ctx = d->max_ctx;
   a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
   a.drop_last = (d->flags & DEC_TEST_DROP_SPLIT) ? 1 : 0;
-  int nw, lds;
-  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, 1, d->max_ctx, d->attn_chunk, &a.chunk, &a.nsplit, &nw,
-                 &lds);
+  int nw, kind;
+  attn_plan_of(d, &a.chunk, &a.nsplit, &nw, &kind);
   return launched(dec::launch_attn_o(a, s), "attn_o");
 }
 
@@ -340,9 +355,8 @@ const char* dec_last_error(void) { return g_err; }
 
 int64_t dec_attn_part_floats(const dec_layer_desc* d) {
   if (check_desc(d)) return -1;
-  int chunk, ns, nw, lds;
-  dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx, d->attn_chunk,
-                 &chunk, &ns, &nw, &lds);
+  int chunk, ns, nw, kind;
+  attn_plan_of(d, &chunk, &ns, &nw, &kind);
   return int64_t(d->n_q_heads) * ns * (d->head_dim + 2);
 }
 

@@ -184,70 +184,93 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   attn_finish<D, G, NW>(a, j, s, ns, AttnShared{&ored[0][0][0], &stat[0][0], &cwts[0][0], cden, caccs, &role});
 }
 
-void attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit,
-               int* waves, int* lds) {
-  // The streaming kernel (dec_attn_stream.hip) whenever its chunk's values
-  // fit in LDS: by default about one workgroup per compute unit over the
-  // whole cache (at most 64 splits per kv head), chunks a multiple of 8
-  // positions.
-  const int cmax = attn_lds_max_chunk(n_q, n_kv, head_dim, kvtype);
-  if (chunk_req <= 0 && cmax > 0) {
-    int splits = kLdsTargetGroups / n_kv;
-    splits = splits < 1 ? 1 : splits > 64 ? 64 : splits;
-    int c = (max_ctx + splits - 1) / splits;
-    c = (c + 7) / 8 * 8;
-    if (c > cmax) c = cmax;
-    // only mid-length chunks stream: a stream of a few rows never fills
-    // (the batched kernel's single pass has fewer barriers), and with
-    // 260+ rows per workgroup the batched kernel's three times as many
-    // shorter workgroups balance the compute units better (measured: 7B- and
-    // 9B-shaped 4-bit caches, 34 MB per layer, 8.6 -> 10.2 us and 15.8 ->
-    // 17.4 us streamed)
-    if (c >= kStreamMinRows && c <= kStreamMaxRows && (max_ctx + c - 1) / c <= kSplitMax) {
-      *chunk = c;
-      *nsplit = (max_ctx + c - 1) / c;
-      *waves = kLdsWaves;
-      *lds = 1;
-      return;
+// splits per kv head for about one workgroup per compute unit (at most 64)
+static int target_splits(int n_kv) {
+  int splits = kLdsTargetGroups / n_kv;
+  return splits < 1 ? 1 : splits > 64 ? 64 : splits;
+}
+
+// default chunk of the batched kernel: about one workgroup per compute unit
+// over the whole cache, a multiple of 16 rows and no longer than one batch
+// of rows in flight
+static int batched_default_chunk(int n_kv, int head_dim, int kvtype, int max_ctx) {
+  const int lanes_per_row = head_dim * (kvtype == 1 ? 2 : 4) / 16;
+  const int one_batch = (kWave / lanes_per_row) * 4 * 8;
+  const int splits = target_splits(n_kv);
+  int c = (max_ctx + splits - 1) / splits;
+  c = ((c + 15) / 16) * 16;
+  if (c > one_batch) c = one_batch;
+  // bf16 head_dim 128: at most 96 rows, three quarters of a batch (more
+  // splits, shorter chains per workgroup; measured against 128: 9B-shaped
+  // layer at 8320 positions 16.6 -> 16.0 us, 7B-shaped at 2112 positions
+  // 12.3 -> 11.95 us)
+  if (head_dim == 128 && kvtype == 1 && c > 96) c = 96;
+  return c;
+}
+
+// default chunk of the streaming and wave-local kernels: about one
+// workgroup per compute unit over the whole cache, a multiple of 8 rows, at
+// most cmax
+static int wide_default_chunk(int n_kv, int max_ctx, int cmax) {
+  const int splits = target_splits(n_kv);
+  int c = (max_ctx + splits - 1) / splits;
+  c = (c + 7) / 8 * 8;
+  return c > cmax ? cmax / 8 * 8 : c;
+}
+
+bool attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int kind_req, int* chunk,
+               int* nsplit, int* waves, int* kind) {
+  const int smax = attn_lds_max_chunk(n_q, n_kv, head_dim, kvtype);   // streaming kernel: 0 if none fits
+  const int lmax = kvtype == 1 ? attn_local_max_chunk(head_dim, kvtype) : 0;
+  int k = kind_req;
+  if (k == kAttnDefault) {
+    if (chunk_req > 0) {
+      // a requested chunk: the streaming kernel when its values fit in LDS
+      k = chunk_req <= smax ? kAttnStream : kAttnBatched;
+    } else if (lmax > 0 && n_q == n_kv) {
+      // one query head per kv head: the wave-local kernel (its scores and
+      // sums are a quarter of a four-head group's; measured on the 7B-shaped
+      // bf16 layer: 385.4 -> 397.0 tok/s against the batched kernel). With
+      // four heads per kv head it lost (9B-shaped bf16 layer 327.8 -> 323.0,
+      // 4-bit 490.8 -> 478.9, 1B-shaped 1686.8 -> 1667.8): their arithmetic
+      // waits for the rows, where the streaming kernel scores as they arrive
+      // and the batched kernel's smaller workgroups overlap it.
+      k = kAttnLocal;
+    } else {
+      // only mid-length chunks stream: a stream of a few rows never fills
+      // (the batched kernel's single pass has fewer barriers), and with
+      // 260+ rows per workgroup the batched kernel's three times as many
+      // shorter workgroups balance the compute units better (measured:
+      // 7B- and 9B-shaped 4-bit caches, 34 MB per layer, 8.6 -> 10.2 us
+      // and 15.8 -> 17.4 us streamed)
+      const int c = smax > 0 ? wide_default_chunk(n_kv, max_ctx, smax) : 0;
+      k = (c >= kStreamMinRows && c <= kStreamMaxRows) ? kAttnStream : kAttnBatched;
     }
   }
-  if (chunk_req > 0 && chunk_req <= cmax && (max_ctx + chunk_req - 1) / chunk_req <= kSplitMax) {
-    *chunk = chunk_req;
-    *nsplit = (max_ctx + chunk_req - 1) / chunk_req;
-    *waves = kLdsWaves;
-    *lds = 1;
-    return;
+  int c = 0, w = 4;
+  bool ok = true;
+  if (k == kAttnLocal) {
+    c = chunk_req > 0 ? chunk_req : wide_default_chunk(n_kv, max_ctx, lmax);
+    ok = lmax > 0 && c <= lmax;
+    w = kLocalWaves;
+  } else if (k == kAttnStream) {
+    c = chunk_req > 0 ? chunk_req : wide_default_chunk(n_kv, max_ctx, smax);
+    ok = smax > 0 && c <= smax;
+    w = kLdsWaves;
+  } else {
+    k = kAttnBatched;
+    c = chunk_req > 0 ? chunk_req : batched_default_chunk(n_kv, head_dim, kvtype, max_ctx);
+    const int cmin = (max_ctx + kSplitMax - 1) / kSplitMax;
+    if (c < cmin) c = cmin;
+    if (c < 16) c = 16;
+    if (c > kChunkMax) c = kChunkMax;
   }
-  // Otherwise the batched kernel above: rows held in registers in batches
-  // (a requested chunk whose values do not fit in LDS).
-  int c = chunk_req;
-  int nw = 4;
-  if (c <= 0) {
-    // about one workgroup per compute unit over the whole cache (at most
-    // 64 splits per kv head), chunks a multiple of 16 rows and no longer
-    // than one batch of rows in flight
-    const int lanes_per_row = head_dim * (kvtype == 1 ? 2 : 4) / 16;
-    const int one_batch = (kWave / lanes_per_row) * 4 * 8;
-    int splits = 256 / n_kv;
-    if (splits > 64) splits = 64;
-    if (splits < 1) splits = 1;
-    c = (max_ctx + splits - 1) / splits;
-    c = ((c + 15) / 16) * 16;
-    if (c > one_batch) c = one_batch;
-    // bf16 head_dim 128: at most 96 rows, three quarters of a batch (more
-    // splits, shorter chains per workgroup; measured against 128: 9B-shaped
-    // layer at 8320 positions 16.6 -> 16.0 us, 7B-shaped at 2112 positions
-    // 12.3 -> 11.95 us)
-    if (head_dim == 128 && kvtype == 1 && c > 96) c = 96;
-  }
-  const int cmin = (max_ctx + kSplitMax - 1) / kSplitMax;
-  if (c < cmin) c = cmin;
-  if (c < 16) c = 16;
-  if (c > kChunkMax) c = kChunkMax;
+  if (c < 1) c = 1;
   *chunk = c;
   *nsplit = (max_ctx + c - 1) / c;
-  *waves = nw;
-  *lds = 0;
+  *waves = w;
+  *kind = k;
+  return ok && *nsplit <= kSplitMax;
 }
 
 template <int D, int KVT, int NW, bool VL>
@@ -280,7 +303,8 @@ static hipError_t go_attn_waves(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
-  if (a.lds) return launch_attn_lds(a, s);
+  if (a.kind == kAttnStream) return launch_attn_lds(a, s);
+  if (a.kind == kAttnLocal) return launch_attn_local(a, s);
   if (a.nsplit > kSplitMax || a.chunk > kChunkMax) return hipErrorInvalidValue;
   if (a.d == 64) return a.kvtype == 1 ? go_attn_waves<64, 1>(a, s) : go_attn_waves<64, 0>(a, s);
   if (a.d == 128) return a.kvtype == 1 ? go_attn_waves<128, 1>(a, s) : go_attn_waves<128, 0>(a, s);

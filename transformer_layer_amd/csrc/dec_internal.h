@@ -97,18 +97,34 @@ struct AttnArgs {
   uint32_t* err;
   int nq, nkv, d, max_ctx, chunk, nsplit, kvtype;
   int waves;           // waves per workgroup (4 or 8)
-  int lds;             // 1: the streaming kernel (dec_attn_stream.hip), values staged in LDS
+  int kind;            // kAttnBatched, kAttnStream or kAttnLocal: which kernel runs
   int no_wait;         // combiners give up at once when splits are missing (failure-path tests)
   int partials_only;   // write the splits' partials and stop (the output projection combines them)
   int drop_last;       // test-only fault: the combine leaves out the last split (two or more splits)
   int null_kernel;
 };
 
-// attention chunk (positions per split), split count, waves per workgroup
-// and kernel (lds = 1: the streaming kernel) for a shape
-void attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int* chunk, int* nsplit,
-               int* waves, int* lds);
+// The attention kernels: batched (dec_attn.hip: rows in registers in
+// batches, one softmax per workgroup through LDS), streaming
+// (dec_attn_stream.hip: keys scored as they arrive, values staged in LDS)
+// and wave-local (dec_attn_local.hip: every row requested at launch, a
+// softmax per wave, bf16 caches).
+constexpr int kAttnDefault = -1, kAttnBatched = 0, kAttnStream = 1, kAttnLocal = 2;
+
+// Attention chunk (positions per split), split count, waves per workgroup
+// and kernel for a shape. kind_req picks the kernel (kAttnDefault: the
+// library's choice for the shape), chunk_req the chunk (0: the kernel's
+// default). False if the requested kernel cannot run the shape or chunk.
+bool attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int kind_req, int* chunk,
+               int* nsplit, int* waves, int* kind);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+// The wave-local kernel: kLocalWaves waves per workgroup, each with at most
+// kLocalMaxSteps row loads of keys and of values in flight per lane.
+constexpr int kLocalWaves = 8;
+constexpr int kLocalMaxSteps = 9;
+int attn_local_max_chunk(int head_dim, int kvtype);
+hipError_t launch_attn_local(const AttnArgs& a, hipStream_t s);
 
 // The streaming attention kernel: eight waves per workgroup; the longest
 // chunk (a multiple of its row step) whose values, scores and scratch fit in

@@ -20,6 +20,10 @@ DEC_NO_FUSE_QKV = 0x4
 DEC_NO_FUSE_FFN = 0x8
 DEC_NO_FUSE_ATTN_O = 0x10
 DEC_DETERMINISTIC = 0x20
+DEC_ATTN_KERNEL_MASK = 0x3000
+DEC_ATTN_BATCHED = 0x1000
+DEC_ATTN_STREAM = 0x2000
+DEC_ATTN_LOCAL = 0x3000
 DEC_TEST_NO_WAIT = 0x100
 DEC_TEST_SKIP_ROPE = 0x200
 DEC_TEST_APPEND_NEXT = 0x400
@@ -27,7 +31,7 @@ DEC_TEST_DROP_SPLIT = 0x800
 DEC_ERR_POS = 0x1
 DEC_ERR_TOKEN = 0x2
 DEC_ERR_SYNC = 0x4
-ABI_VERSION = 3
+ABI_VERSION = 4
 DEC_COUNTER_STRIDE = 16
 DEC_STATIC_SCRATCH_BYTES = 4 << 20
 
