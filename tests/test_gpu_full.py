@@ -139,7 +139,7 @@ def test_fused_matches_unfused_at_full_shape(gpu, name):
     hidden states and caches agree bit for bit. bf16: the fused output
     projection adds the kv head groups' shares to x with float atomics in no
     fixed order, so the two agree within float32 reordering (and a bf16
-    cache value may round the other way)."""
+    cache value may round the other way, so cache vectors are compared in L2)."""
     cfg = synth.CONFIGS[name]
     nl, nsteps = 2, 3
     toks = synth.tokens(cfg)
@@ -171,12 +171,17 @@ def test_fused_matches_unfused_at_full_shape(gpu, name):
         return
     worst = max(rel_l2(xa[s, l], xb[s, l]) for s in range(nsteps) for l in range(1, nl + 1))
     assert worst <= 1e-5, f"{name}: fused vs per-op relative L2 {worst:.3e}"
-    # caches: prefill and unwritten slots identical, decoded slots within one bf16 step
+    # caches: prefill and unwritten slots identical; each decoded head vector
+    # within bf16 rounding of the other. Compared per vector, not per value:
+    # a value that is small next to its vector (cancellation in k = W u) can
+    # move by several of its own bf16 steps when x moves by float32
+    # reordering, while the vector moves by about one step in L2.
     assert torch.equal(Ka[:, :, : cfg.ctx], Kb[:, :, : cfg.ctx]) and torch.equal(Va[:, :, : cfg.ctx], Vb[:, :, : cfg.ctx])
     for A, B in ((Ka, Kb), (Va, Vb)):
-        a = A[:, :, cfg.ctx: cfg.ctx + nsteps].view(torch.bfloat16).float()
-        b = B[:, :, cfg.ctx: cfg.ctx + nsteps].view(torch.bfloat16).float()
-        assert bool(((a - b).abs() <= a.abs() * 2.0 ** -7).all()), f"{name}: decoded cache slots differ"
+        a = A[:, :, cfg.ctx: cfg.ctx + nsteps].view(torch.bfloat16).double()
+        b = B[:, :, cfg.ctx: cfg.ctx + nsteps].view(torch.bfloat16).double()
+        rel = (a - b).norm(dim=-1) / a.norm(dim=-1)
+        assert float(rel.max()) <= 2.0 ** -8, f"{name}: decoded cache vectors differ ({float(rel.max()):.2e})"
 
 
 GREEDY = sorted(os.path.basename(p)[len("greedy_"):-len(".json")] for p in glob.glob(os.path.join(GOLD, "greedy_*.json")))
