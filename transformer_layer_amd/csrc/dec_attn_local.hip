@@ -75,8 +75,9 @@ __global__ __launch_bounds__(NW * 64) void attn_local_kernel(AttnArgs a) {
   // row of this wave, then every value row. Loads complete in order, so
   // the queries arrive first, each key row can be scored as it arrives and
   // each value row summed as it arrives. The queries go through this
-  // wave's slice of LDS (the slice its output takes later): every lane
-  // requesting its own slice of every head's query asked for 32x the 2 KB.
+  // wave's slice of LDS (the slice its output takes later): with every lane
+  // requesting its own slice of every head's query, a workgroup asked for
+  // the kv head's queries 32 times over (four heads of 128, eight waves).
   constexpr int NQ4 = G * D / 4;                  // float4s of the kv head's queries
   constexpr int QPL = (NQ4 + kWave - 1) / kWave;  // per lane
   float4 qraw[QPL];
