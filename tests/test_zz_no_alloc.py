@@ -52,10 +52,11 @@ def _static_state(st):
 
 CASES = [
     # (workload, flags, position, x compared bit for bit)
-    ("C4", 0, 4100, False),                   # 22 splits of 192 positions: the largest partials here
+    ("C5", 0, 8200, True),                    # 4-bit weights, in-kernel combine (88 splits): the largest partials
+    ("C4", 0, 4100, False),                   # streaming attention, 32 splits, combine in the O projection
+    ("C3", 0, 2060, False),                   # wave-local attention, 8 splits of 272 positions
     ("C1", 0, 17, True),                      # smaller: f32, two splits
     ("C4", L.DEC_DETERMINISTIC, 4099, True),
-    ("C5", 0, 8200, True),                    # 4-bit weights, in-kernel combine (87 splits)
     ("C2", 0, 515, False),
     ("C1", L.DEC_UNFUSED, 19, True),          # the per-op intermediates in the static array
 ]
