@@ -28,6 +28,7 @@ from .ref import (  # noqa: F401
     bf16_bits_to_f64,
     dequant,
     q4_dequant,
+    quantize_i8,
     rmsnorm,
     rope,
     rope_inv_freq,

@@ -6,6 +6,7 @@ this module. It shares no code with the GPU path.
 Page citations name the page title and section:
 
 * [P1] "RDNA4 Decode Kernel Fusion: Pipeline Barriers, Not Launches, Are the Win"
+* [P2] "Vulkan Command Buffer Reuse vs CUDA Graphs: RDNA4 Decode Overhead"
 * [P3] "backend-specific kernel fusion" (gearjunkie.de)
 * [P4] "Kernel fusion and block bridging" (jitllm docs)
 
@@ -22,6 +23,10 @@ of the repository):
 * the cache stores rotated k and plain v rounded to the cache type; for a
   bf16 cache the value is first rounded to fp32 (the GPU path's working
   precision) and then to bf16, both round-to-nearest-even;
+* int8 cache (the pages name "a leaner KV cache" as a bytes-per-token lever
+  and give no scheme): one binary32 scale per cached row (one kv head at one
+  position, k and v separately) and symmetric codes in [-127, 127], every
+  decision taken in binary32 (quantize_i8);
 * SwiGLU: h = silu(gate) * up with silu(z) = z / (1 + exp(-z));
 * 4-bit weights: w = scale * code, code a two's-complement nibble, element 2i
   the low nibble of byte i, one fp16 scale per 32 consecutive inputs;
@@ -143,10 +148,37 @@ def round_to_cache(v: np.ndarray, kvtype: str) -> np.ndarray:
     return out.astype(np.uint16)
 
 
-def cache_values(c: np.ndarray, kvtype: str, dtype) -> np.ndarray:
-    """Cache storage (fp32 values or bf16 bit patterns) as real values."""
+def quantize_i8(v: np.ndarray) -> tuple:
+    """The int8 cache entry of rows ``v[..., d]`` (each row one kv head's k
+    or v at one position; [P2] "Vulkan Command Buffer Reuse vs CUDA Graphs:
+    RDNA4 Decode Overhead", section "What I am building next": a leaner KV
+    cache as a bytes-per-token lever, scheme not given).
+
+    x = v rounded to binary32; m = max |x| over the row; scale = m / 127 and
+    inv = 127 / m, each a binary32 division rounded to nearest; code = the
+    binary32 product x * inv rounded to the nearest integer (ties to even),
+    clamped to [-127, 127]. A row of zeros has scale 0 and codes 0. Returns
+    (codes int8 ``[..., d]``, scales float32 ``[...]``); the cached value is
+    code * scale.
+    """
+    x = np.asarray(v).astype(np.float32)
+    m = np.abs(x).max(axis=-1)
+    zero = m == 0
+    msafe = np.where(zero, np.float32(1), m).astype(np.float32)
+    scale = np.where(zero, np.float32(0), msafe / np.float32(127)).astype(np.float32)
+    inv = np.where(zero, np.float32(0), np.float32(127) / msafe).astype(np.float32)
+    prod = (x * inv[..., None]).astype(np.float32)
+    codes = np.clip(np.rint(prod), -127, 127).astype(np.int8)
+    return codes, scale
+
+
+def cache_values(c: np.ndarray, kvtype: str, dtype, scales=None) -> np.ndarray:
+    """Cache storage (fp32 values, bf16 bit patterns, or int8 codes with
+    their per-row scales) as real values."""
     if kvtype == "f32":
         return c.astype(dtype)
+    if kvtype == "i8":
+        return (c.astype(np.float64) * np.asarray(scales, dtype=np.float64)[..., None]).astype(dtype)
     return bf16_bits_to_f64(c).astype(dtype)
 
 
@@ -203,12 +235,15 @@ class Oracle:
         n_elem = sum(int(np.prod(v.shape)) for lw in layers for v in lw.values())
         self.keep = (n_elem * 8 <= (64 << 20)) if keep_dequant is None else keep_dequant
         self._deq = {}
-        cdt = np.float32 if cfg.kvtype == "f32" else np.uint16
+        cdt = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}[cfg.kvtype]
         shape = (cfg.n_kv_heads, cfg.max_ctx, cfg.head_dim)
-        # the cache in its storage encoding, and the same entries decoded to
-        # real values (written together; attention reads the decoded copy)
+        # the cache in its storage encoding (an int8 cache also keeps one
+        # scale per row), and the same entries decoded to real values
+        # (written together; attention reads the decoded copy)
         self.K = [np.zeros(shape, dtype=cdt) for _ in layers]
         self.V = [np.zeros(shape, dtype=cdt) for _ in layers]
+        self.Ks = [np.zeros(shape[:2], dtype=np.float32) for _ in layers]
+        self.Vs = [np.zeros(shape[:2], dtype=np.float32) for _ in layers]
         self.Kd = [np.zeros(shape, dtype=self.dtype) for _ in layers]
         self.Vd = [np.zeros(shape, dtype=self.dtype) for _ in layers]
 
@@ -253,8 +288,11 @@ class Oracle:
         n = K.data.shape[1]
         self.K[l][:, :n] = K.data
         self.V[l][:, :n] = V.data
-        self.Kd[l][:, :n] = cache_values(self.K[l][:, :n], self.cfg.kvtype, self.dtype)
-        self.Vd[l][:, :n] = cache_values(self.V[l][:, :n], self.cfg.kvtype, self.dtype)
+        if self.cfg.kvtype == "i8":
+            self.Ks[l][:, :n] = K.scales
+            self.Vs[l][:, :n] = V.scales
+        self.Kd[l][:, :n] = cache_values(self.K[l][:, :n], self.cfg.kvtype, self.dtype, self.Ks[l][:, :n])
+        self.Vd[l][:, :n] = cache_values(self.V[l][:, :n], self.cfg.kvtype, self.dtype, self.Vs[l][:, :n])
 
     # -- the layer's steps, in the order of [P1]
     def qkv_rope_append(self, l: int, x: np.ndarray, p: int) -> np.ndarray:
@@ -269,11 +307,21 @@ class Oracle:
         v = y[c.q_dim + c.kv_dim:].reshape(c.n_kv_heads, d)
         q = rope(q, p, c.rope_theta)
         k = rope(k, p, c.rope_theta)
-        self.K[l][:, p, :] = round_to_cache(k, c.kvtype)
-        self.V[l][:, p, :] = round_to_cache(v, c.kvtype)
-        self.Kd[l][:, p, :] = cache_values(self.K[l][:, p, :], c.kvtype, self.dtype)
-        self.Vd[l][:, p, :] = cache_values(self.V[l][:, p, :], c.kvtype, self.dtype)
+        self.append(l, k, v, p)
         return q
+
+    def append(self, l: int, k: np.ndarray, v: np.ndarray, p: int) -> None:
+        """Store the rotated k and plain v ``[n_kv, d]`` at position p of
+        layer l, in the cache's encoding."""
+        c = self.cfg
+        if c.kvtype == "i8":
+            self.K[l][:, p, :], self.Ks[l][:, p] = quantize_i8(k)
+            self.V[l][:, p, :], self.Vs[l][:, p] = quantize_i8(v)
+        else:
+            self.K[l][:, p, :] = round_to_cache(k, c.kvtype)
+            self.V[l][:, p, :] = round_to_cache(v, c.kvtype)
+        self.Kd[l][:, p, :] = cache_values(self.K[l][:, p, :], c.kvtype, self.dtype, self.Ks[l][:, p])
+        self.Vd[l][:, p, :] = cache_values(self.V[l][:, p, :], c.kvtype, self.dtype, self.Vs[l][:, p])
 
     def attention(self, l: int, q: np.ndarray, p: int) -> np.ndarray:
         """Attention of q over cache positions 0..p of layer l; returns the

@@ -65,7 +65,7 @@ class DecodeConfig:
         return asdict(self)
 
 
-_ELEM = {"f32": 4.0, "bf16": 2.0, "q4": 0.5 + 2.0 / 32.0}
+_ELEM = {"f32": 4.0, "bf16": 2.0, "q4": 0.5 + 2.0 / 32.0, "i8": 1.0}
 
 
 def elem_bytes(t: str) -> float:
@@ -87,10 +87,11 @@ def layer_weight_bytes(c: DecodeConfig) -> dict:
 
 
 def kv_bytes(c: DecodeConfig, length: int) -> dict:
-    """KV bytes one layer reads (over `length` positions) and writes."""
-    e = elem_bytes(c.kvtype)
-    return {"read": 2 * c.n_kv_heads * c.head_dim * length * e,
-            "write": 2 * c.n_kv_heads * c.head_dim * e}
+    """KV bytes one layer reads (over `length` positions) and writes (an
+    int8 cache row also carries its 4-byte scale)."""
+    row = c.head_dim * elem_bytes(c.kvtype) + (4 if c.kvtype == "i8" else 0)
+    return {"read": 2 * c.n_kv_heads * row * length,
+            "write": 2 * c.n_kv_heads * row}
 
 
 def head_bytes(c: DecodeConfig) -> float:

@@ -80,7 +80,8 @@ class Stored:
 
     kind "f32": ``data`` is float32; kind "bf16": ``data`` is uint16 bf16 bit
     patterns; kind "q4": ``data`` is uint8 nibbles ``[rows, cols/2]`` and
-    ``scales`` float16 ``[rows, cols/32]``.
+    ``scales`` float16 ``[rows, cols/32]``; kind "i8" (cache rows): ``data``
+    is int8 codes ``[..., d]`` and ``scales`` float32 ``[...]``, one per row.
     """
     kind: str
     data: np.ndarray
@@ -179,6 +180,9 @@ def prefill(cfg: DecodeConfig, layer: int) -> tuple:
     """
     std = 0.02 * float(np.sqrt(cfg.hidden))
     rows = cfg.n_kv_heads * cfg.ctx
+    if cfg.kvtype == "i8":
+        return tuple(_i8_rows((cfg.seed, layer, tid), cfg.n_kv_heads, cfg.ctx, cfg.head_dim, std)
+                     for tid in (KPRE, VPRE))
     out = []
     for tid in (KPRE, VPRE):
         st = _normal_rows((cfg.seed, layer, tid), rows, cfg.head_dim, std, 0.0, cfg.kvtype)
@@ -232,7 +236,19 @@ def rand_norm(key, n: int, kind: str) -> Stored:
     return _norm(tuple(key), n, kind)
 
 
+def _i8_rows(key, n_kv: int, length: int, d: int, std: float) -> Stored:
+    """int8 cache rows: codes uniform in [-127, 127] and one positive scale
+    per row, drawn so that the values have about the given std (a uniform
+    code has std 73.3)."""
+    rng = _rng(tuple(key), 0, 1)
+    codes = rng.integers(-127, 128, size=(n_kv, length, d), dtype=np.int16).astype(np.int8)
+    scales = (np.float32(std / 73.3) * rng.uniform(0.75, 1.25, size=(n_kv, length))).astype(np.float32)
+    return Stored("i8", codes, scales)
+
+
 def rand_cache(key, n_kv: int, length: int, d: int, kind: str, std: float) -> Stored:
     """Seeded cache contents ``[n_kv, length, d]`` in storage encoding (test inputs)."""
+    if kind == "i8":
+        return _i8_rows(key, n_kv, length, d, std)
     st = _normal_rows(tuple(key), n_kv * length, d, std, 0.0, kind)
     return Stored(st.kind, st.data.reshape(n_kv, length, d))

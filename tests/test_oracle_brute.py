@@ -115,7 +115,10 @@ def _pins_that_should_fail():
         pins.test_attention_matches_torch_sdpa_gqa,
         pins.test_silu_fixture_and_swiglu_zero,
         pins.test_integer_exact_append,
-        lambda: pins.test_decode_equals_dense_causal_forward("f32", 4, 2),
+        lambda: pins.test_decode_equals_dense_causal_forward("f32", 4, 2, "f32"),
+        pins.test_i8_cache_row_fixture,
+        pins.test_i8_cache_rows_round_to_nearest_step,
+        lambda: pins.test_decode_equals_dense_causal_forward("bf16", 8, 2, "i8"),
     ]
 
 
@@ -171,6 +174,28 @@ def _round_truncate(v, kvtype):
     return (f.view(np.uint32) >> 16).astype(np.uint16)
 
 
+def _i8_step_128(v):
+    x = np.asarray(v).astype(np.float32)
+    m = np.abs(x).max(axis=-1)
+    scale = (m / np.float32(128)).astype(np.float32)
+    inv = np.where(m == 0, np.float32(0), np.float32(128) / np.where(m == 0, np.float32(1), m)).astype(np.float32)
+    return np.clip(np.rint(x * inv[..., None]), -127, 127).astype(np.int8), scale
+
+
+def _i8_truncate(v):
+    codes, scale = _orig["quantize_i8"](v)
+    x = np.asarray(v).astype(np.float32)
+    inv = np.where(scale == 0, np.float32(0), np.float32(1) / np.where(scale == 0, np.float32(1), scale))
+    return np.clip(np.trunc(x * inv[..., None]), -127, 127).astype(np.int8), scale
+
+
+def _i8_one_scale_per_head(v):
+    # one scale for the whole [n_kv, d] block instead of one per row
+    x = np.asarray(v)
+    codes, scale = _orig["quantize_i8"](x.reshape(1, -1))
+    return codes.reshape(x.shape), np.full(x.shape[:-1], scale[0], np.float32)
+
+
 _orig = {}
 
 
@@ -184,6 +209,9 @@ def _mutations():
         "sigmoid for silu": [("silu", _silu_sigmoid)],
         "nibbles swapped": [("q4_dequant", _q4_swapped)],
         "bf16 truncation": [("round_to_cache", _round_truncate)],
+        "int8 step of 1/128": [("quantize_i8", _i8_step_128)],
+        "int8 codes truncated": [("quantize_i8", _i8_truncate)],
+        "int8 scale per block, not per row": [("quantize_i8", _i8_one_scale_per_head)],
     }
 
 
@@ -196,7 +224,7 @@ def test_pins_pass_without_a_planted_mistake():
 
 @pytest.mark.parametrize("name", list(_mutations()))
 def test_planted_mistake_fails_a_pin(name, monkeypatch):
-    for fn in ("rope", "rmsnorm", "attend", "silu", "q4_dequant", "round_to_cache"):
+    for fn in ("rope", "rmsnorm", "attend", "silu", "q4_dequant", "round_to_cache", "quantize_i8"):
         _orig[fn] = getattr(ref, fn)
     for fn, repl in _mutations()[name]:
         monkeypatch.setattr(ref, fn, repl)
@@ -230,7 +258,7 @@ def test_planted_off_by_one_and_missing_residual_fail_a_pin(monkeypatch):
         with monkeypatch.context() as m:
             m.setattr(ref.Oracle, attr, repl)
             failed = 0
-            for pin in (lambda: pins.test_decode_equals_dense_causal_forward("f32", 4, 2),
+            for pin in (lambda: pins.test_decode_equals_dense_causal_forward("f32", 4, 2, "f32"),
                         pins.test_integer_exact_append):
                 try:
                     pin()

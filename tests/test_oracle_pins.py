@@ -192,6 +192,51 @@ def test_silu_matches_torch():
 
 # ------------------------------------------------------------------ whole layer
 
+def test_i8_cache_row_fixture():
+    """Hand-computed int8 cache rows: a row whose largest magnitude is 127
+    has scale 1 and inverse 1, so its codes are the values rounded to the
+    nearest integer, ties to even; largest magnitude 254: scale 2, inverse
+    0.5, both exact; a row of zeros: scale 0, codes 0."""
+    codes, scale = oracle.quantize_i8(np.array([[127.0, -63.5, 0.5, 1.5, -2.5, 0.0, 2.49, -126.6]]))
+    assert scale[0] == np.float32(1.0)
+    assert codes.tolist() == [[127, -64, 0, 2, -2, 0, 2, -127]]
+    codes, scale = oracle.quantize_i8(np.array([[-254.0, 3.0, 5.0, 1.0]]))
+    assert scale[0] == np.float32(2.0)
+    assert codes.tolist() == [[-127, 2, 2, 0]]      # 1.5 -> 2, 2.5 -> 2, 0.5 -> 0
+    codes, scale = oracle.quantize_i8(np.zeros((3, 8)))
+    assert (codes == 0).all() and (scale == 0).all()
+    got = cache_values(np.array([[3, -127]], np.int8), "i8", np.float64, np.array([0.5], np.float32))
+    assert got.tolist() == [[1.5, -63.5]]
+
+
+def test_i8_cache_rows_round_to_nearest_step():
+    """On 4000 random rows of 128 (magnitudes 0.01 to 100): the scale is the
+    row maximum / 127 in binary32; the largest element becomes +-127; away
+    from a half (1e-4, the binary32 product's error), every code is the
+    nearest integer to x * 127 / m computed exactly; the value code * scale
+    is within half a step of x; negating a row negates its codes, and
+    scaling it by 8 scales only its scale."""
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((4000, 128)) * rng.uniform(0.01, 100, (4000, 1))
+    codes, scale = oracle.quantize_i8(v)
+    x = v.astype(np.float32).astype(np.float64)
+    m = np.abs(x).max(1)
+    assert np.array_equal(scale, (m / 127).astype(np.float32))
+    rows = np.arange(len(v))
+    i = np.abs(x).argmax(1)
+    assert np.array_equal(codes[rows, i], (127 * np.sign(x[rows, i])).astype(np.int8))
+    exact = x * 127.0 / m[:, None]
+    far = np.abs(exact - np.floor(exact) - 0.5) > 1e-4
+    assert far.mean() > 0.99
+    assert np.array_equal(codes[far], np.rint(exact[far]).astype(np.int8))
+    err = np.abs(codes * scale[:, None].astype(np.float64) - x)
+    assert (err <= 0.5 * scale[:, None].astype(np.float64) * (1 + 1e-5)).all()
+    c2, s2 = oracle.quantize_i8(-v)
+    assert np.array_equal(c2, -codes) and np.array_equal(s2, scale)
+    c3, s3 = oracle.quantize_i8(v * 8.0)
+    assert np.array_equal(c3, codes) and np.array_equal(s3, scale * np.float32(8))
+
+
 def _integer_layer_cfg():
     return synth.tiny(hidden=8, n_q_heads=2, n_kv_heads=1, head_dim=4, ffn=16,
                       rms_eps=0.0, ctx=0, steps=1)
@@ -237,6 +282,14 @@ def _dense_causal_forward(cfg, layers, X):
 
     def to_cache(t):
         t = t.to(torch.float32)
+        if cfg.kvtype == "i8":
+            # per row (kv head, position): binary32 scale and inverse, codes
+            # rounded half to even by torch.round, clamped
+            m = t.abs().amax(-1, keepdim=True)
+            inv = torch.where(m == 0, torch.zeros_like(m), torch.tensor(127.0, dtype=torch.float32) / m)
+            code = torch.round(t * inv).clamp(-127, 127)
+            scale = torch.where(m == 0, torch.zeros_like(m), m / torch.tensor(127.0, dtype=torch.float32))
+            return code.to(torch.float64) * scale.to(torch.float64)
         if cfg.kvtype == "bf16":
             t = t.to(torch.bfloat16)
         return t.to(torch.float64)
@@ -261,9 +314,9 @@ def _dense_causal_forward(cfg, layers, X):
     return x.numpy()
 
 
-@pytest.mark.parametrize("kind,nq,nkv", [("f32", 4, 4), ("f32", 4, 2), ("bf16", 8, 2), ("q4", 4, 1)])
-def test_decode_equals_dense_causal_forward(kind, nq, nkv):
-    kv = "f32" if kind == "f32" else "bf16"
+@pytest.mark.parametrize("kind,nq,nkv,kv", [("f32", 4, 4, "f32"), ("f32", 4, 2, "f32"), ("bf16", 8, 2, "bf16"),
+                                            ("q4", 4, 1, "bf16"), ("bf16", 8, 2, "i8"), ("q4", 4, 2, "i8")])
+def test_decode_equals_dense_causal_forward(kind, nq, nkv, kv):
     cfg = synth.tiny(n_layers=2, hidden=64, n_q_heads=nq, n_kv_heads=nkv, head_dim=16, ffn=96,
                      wtype=kind, ntype="f32" if kind == "f32" else "bf16", kvtype=kv,
                      rope_theta=10000.0, ctx=0, steps=9, seed=21)
