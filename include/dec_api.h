@@ -57,9 +57,9 @@
 extern "C" {
 #endif
 
-#define DEC_ABI_VERSION 4
+#define DEC_ABI_VERSION 5
 
-enum dec_dtype { DEC_F32 = 0, DEC_BF16 = 1, DEC_Q4 = 2 };
+enum dec_dtype { DEC_F32 = 0, DEC_BF16 = 1, DEC_Q4 = 2, DEC_I8 = 3 };
 
 enum dec_status {
   DEC_OK = 0,
@@ -136,7 +136,8 @@ typedef struct {
   float rms_eps;       /* RMSNorm epsilon, added to mean(x^2) inside the root */
   int32_t wtype;       /* projection weights: DEC_F32 | DEC_BF16 | DEC_Q4 */
   int32_t ntype;       /* norm weights: DEC_F32 | DEC_BF16 */
-  int32_t kvtype;      /* KV cache: DEC_F32 | DEC_BF16 */
+  int32_t kvtype;      /* KV cache: DEC_F32 | DEC_BF16 | DEC_I8 (int8 rows with a float
+                          scale each, head_dim 128; layout at dec_cache_bytes) */
   int32_t attn_chunk;  /* cache positions per attention split; 0 = library default */
   uint32_t flags;      /* DEC_* flags above */
 } dec_layer_desc;
@@ -176,8 +177,9 @@ typedef struct {
   uint32_t* counters;  /* [n_kv * DEC_COUNTER_STRIDE] arrival counters; zero
                           before first use, and the attention kernel leaves
                           them zero */
-  void* k_cache;       /* this layer's keys   [n_kv][max_ctx][d] in kvtype */
-  void* v_cache;       /* this layer's values [n_kv][max_ctx][d] in kvtype */
+  void* k_cache;       /* this layer's keys   [n_kv][max_ctx][d] in kvtype
+                          (DEC_I8: dec_cache_bytes(desc) bytes, see there) */
+  void* v_cache;       /* this layer's values, same layout */
   const int32_t* pos;  /* position p of the token being decoded */
   const float* rope;   /* [max_ctx][d/2][2] (cos, sin) from dec_rope_table */
   uint32_t* err;       /* device error word (bits are OR-ed in) */
@@ -190,6 +192,18 @@ typedef struct {
 
 /* floats needed by dec_layer_state.part for this shape (>= 1). */
 int64_t dec_attn_part_floats(const dec_layer_desc* desc);
+/* Bytes of one layer's k_cache (and of its v_cache), 256-byte aligned
+   sections. DEC_F32/DEC_BF16: the rows [n_kv][max_ctx][d]. DEC_I8 (a leaner
+   KV cache, "Vulkan Command Buffer Reuse vs CUDA Graphs...", section "What I
+   am building next"; the scheme is this library's): int8 codes
+   [n_kv][max_ctx][d], then at byte offset dec_cache_scale_offset one float
+   scale per row [n_kv][max_ctx] (value = code * scale; scale = max|x| / 127,
+   code = x * (127 / max|x|) rounded half to even, in float32), then at
+   dec_cache_stage_offset the newest k (or v) row [n_kv][d] as float32: the
+   QKV step writes it there and the attention quantizes it into slot p. */
+int64_t dec_cache_bytes(const dec_layer_desc* desc);
+int64_t dec_cache_scale_offset(const dec_layer_desc* desc);
+int64_t dec_cache_stage_offset(const dec_layer_desc* desc);
 /* floats needed by dec_layer_state.scratch for the per-op path. */
 int64_t dec_scratch_floats(const dec_layer_desc* desc);
 
@@ -204,7 +218,8 @@ int64_t dec_scratch_floats(const dec_layer_desc* desc);
    Computes u = x / sqrt(mean(x^2) + eps) * attn_norm, y = Wqkv u, rotates
    each q and k head by RoPE at position p (pairs (i, i + d/2), cos/sin from
    the table), writes q (float32) and stores k, v rounded to kvtype
-   (nearest even) at cache position p of every kv head.
+   (nearest even) at cache position p of every kv head (DEC_I8: as float32
+   rows in the cache's stage section; the attention appends them).
    Reads: x, weights, rope, pos. Writes: q, k_cache[:, p], v_cache[:, p], err. */
 int dec_rmsnorm_gemv_qkv_rope(const dec_layer_desc* desc, const dec_layer_weights* w,
                               const dec_layer_state* st, void* stream);
@@ -220,8 +235,10 @@ int dec_rmsnorm_gemv_qkv_rope(const dec_layer_desc* desc, const dec_layer_weight
    Query head h uses kv head h / (n_q/n_kv); scores are scaled by 1/sqrt(d).
    The last arrivals of a kv head combine in a fixed order (each output
    element sums its splits in split order), so repeated runs give the same
-   bits. Reads: q, caches, pos. Writes: attn, part, counters (left zero),
-   err. */
+   bits. DEC_I8 caches: the workgroup whose split holds p quantizes the
+   staged k and v rows into slot p and scores the token from them. Reads:
+   q, caches, pos. Writes: attn, part, counters (left zero), err (and the
+   int8 cache's slot p). */
 int dec_attn_splitk(const dec_layer_desc* desc, const dec_layer_state* st, void* stream);
 
 /* The attention's first half on its own: the same split-K reduction as

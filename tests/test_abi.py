@@ -82,7 +82,8 @@ int main(void) {
   O(dec_layer_state, h) O(dec_layer_state, part) O(dec_layer_state, counters) O(dec_layer_state, k_cache)
   O(dec_layer_state, v_cache) O(dec_layer_state, pos) O(dec_layer_state, rope) O(dec_layer_state, err)
   O(dec_layer_state, scratch)
-  printf("DEC_F32 value %d\nDEC_BF16 value %d\nDEC_Q4 value %d\n", DEC_F32, DEC_BF16, DEC_Q4);
+  printf("DEC_F32 value %d\nDEC_BF16 value %d\nDEC_Q4 value %d\nDEC_I8 value %d\n", DEC_F32, DEC_BF16, DEC_Q4,
+         DEC_I8);
   printf("DEC_UNFUSED value %u\nDEC_NULL_KERNELS value %u\nDEC_TEST_NO_WAIT value %u\n", DEC_UNFUSED,
          DEC_NULL_KERNELS, DEC_TEST_NO_WAIT);
   printf("DEC_NO_FUSE_QKV value %u\nDEC_NO_FUSE_FFN value %u\nDEC_NO_FUSE_ATTN_O value %u\n", DEC_NO_FUSE_QKV,
@@ -113,7 +114,7 @@ def test_struct_layout_matches_a_c_compiler(L, tmp_path):
         name, field, val = ln.split()
         val = int(val)
         if field == "value":
-            want = {"DEC_F32": L.DEC_F32, "DEC_BF16": L.DEC_BF16, "DEC_Q4": L.DEC_Q4,
+            want = {"DEC_F32": L.DEC_F32, "DEC_BF16": L.DEC_BF16, "DEC_Q4": L.DEC_Q4, "DEC_I8": L.DEC_I8,
                     "DEC_UNFUSED": L.DEC_UNFUSED, "DEC_NULL_KERNELS": L.DEC_NULL_KERNELS,
                     "DEC_TEST_NO_WAIT": L.DEC_TEST_NO_WAIT, "DEC_NO_FUSE_QKV": L.DEC_NO_FUSE_QKV,
                     "DEC_NO_FUSE_FFN": L.DEC_NO_FUSE_FFN, "DEC_NO_FUSE_ATTN_O": L.DEC_NO_FUSE_ATTN_O,
@@ -129,7 +130,7 @@ def test_struct_layout_matches_a_c_compiler(L, tmp_path):
         else:
             assert getattr(getattr(L, name), field).offset == val, f"{name}.{field}"
         seen += 1
-    assert seen == 59   # 4 sizes, 33 offsets, 22 constants
+    assert seen == 60   # 4 sizes, 33 offsets, 23 constants
 
 
 # ---- host-side checks (every call below is rejected before any launch)
@@ -193,7 +194,8 @@ def test_buffer_sizes(L, name):
     ("attn_chunk", 300, E_SHAPE, "attn_chunk"),
     ("wtype", 7, E_DTYPE, "wtype"),
     ("ntype", 2, E_DTYPE, "ntype"),             # 4-bit norm weights are not a thing
-    ("kvtype", 2, E_DTYPE, "kvtype"),
+    ("kvtype", 2, E_DTYPE, "kvtype"),           # a 4-bit cache is not a thing either
+    ("kvtype", 4, E_DTYPE, "kvtype"),
 ])
 def test_bad_descriptor_is_rejected(L, field, value, code, word):
     d = desc_of(L, synth.CONFIGS["C4"], **{field: value})
@@ -206,6 +208,8 @@ def test_bad_descriptor_is_rejected(L, field, value, code, word):
     ("DEC_ATTN_LOCAL", {"kvtype": 0}),                        # the wave-local kernel reads bf16 caches only
     ("DEC_ATTN_STREAM", {"kvtype": 0, "n_q_heads": 64, "attn_chunk": 256}),  # f32 values beyond LDS
     ("DEC_ATTN_BATCHED", {"max_ctx": 100000}),                # 391 splits of at most 256 positions
+    ("DEC_ATTN_STREAM", {"kvtype": 3}),                       # an int8 cache is read by the batched kernel only
+    ("DEC_ATTN_LOCAL", {"kvtype": 3}),
 ])
 def test_attention_kernel_that_cannot_run_the_shape_is_refused(L, kernel, over):
     d = desc_of(L, synth.CONFIGS["C4"], flags=getattr(L, kernel), **over)
@@ -224,6 +228,32 @@ def test_every_attention_kernel_plans_the_workloads(L, name):
         assert n > 0, (name, k, L.dec_last_error())
         sizes.append(n)
     assert L.dec_attn_part_floats(desc_of(L, cfg)) in sizes
+
+
+def test_int8_cache_layout_and_shapes(L):
+    """An int8 cache is one buffer per layer: the codes [n_kv, max_ctx, d],
+    one float scale per row from the first 256-byte boundary after them,
+    and the staged newest row (n_kv * d floats) from the next one. Only
+    128-wide heads are accepted; the batched kernel plans every workload
+    shape with it."""
+    for name in ("C3", "C4", "C5"):
+        cfg = synth.CONFIGS[name]
+        d = desc_of(L, cfg, kvtype=L.DEC_I8)
+        codes = cfg.n_kv_heads * cfg.max_ctx * cfg.head_dim
+        up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+        assert L.dec_cache_scale_offset(d) == up(codes)
+        assert L.dec_cache_stage_offset(d) == up(up(codes) + 4 * cfg.n_kv_heads * cfg.max_ctx)
+        assert L.dec_cache_bytes(d) == L.dec_cache_stage_offset(d) + 4 * cfg.n_kv_heads * cfg.head_dim
+        assert L.dec_attn_part_floats(d) > 0, L.dec_last_error()
+        b = desc_of(L, cfg)
+        assert L.dec_cache_bytes(b) == codes * 2
+        lib = L.load()
+        assert lib.dec_cache_scale_offset(ctypes.byref(b)) == -1 and "not int8" in L.dec_last_error()
+        assert lib.dec_cache_stage_offset(ctypes.byref(b)) == -1
+    d = desc_of(L, synth.CONFIGS["C2"], kvtype=L.DEC_I8)   # 64-wide heads
+    assert rc_step(L, d, weights_of(L), state_of(L)) == E_SHAPE
+    assert "int8 cache needs head_dim 128" in L.dec_last_error()
+    assert L.load().dec_cache_bytes(ctypes.byref(d)) == -1
 
 
 def test_null_arguments_are_rejected(L):

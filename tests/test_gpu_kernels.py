@@ -234,6 +234,57 @@ def test_attn_each_kernel(gpu, kernel, d, nq, nkv, max_ctx, positions, chunk):
     assert st.check_err() == 0
 
 
+I8_CASES = [
+    # n_q, n_kv, max_ctx, positions, chunk (int8 cache, head_dim 128, batched kernel)
+    (32, 8, 640, (0, 1, 255, 256, 639), 0),
+    (8, 8, 300, (0, 17, 299), 16),        # one-head groups, one-row splits at 16, 32, ...
+    (16, 2, 700, (699, 350, 48), 48),     # the token alone in its split at 48
+    (16, 2, 2200, (2199,), 100),
+    (32, 4, 4200, (4100, 4101), 0),
+]
+
+
+@pytest.mark.parametrize("nq,nkv,max_ctx,positions,chunk", I8_CASES)
+def test_attn_i8_cache_appends_and_matches_oracle(gpu, nq, nkv, max_ctx, positions, chunk):
+    """int8 cache: the attention quantizes the staged float k and v rows of
+    the token into slot p (codes and scales equal the oracle's, bit for bit:
+    both decide in binary32) and its output matches the oracle's attention
+    over the decoded cache, positions 0..p."""
+    d = 128
+    cfg = synth.tiny(hidden=256, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, ffn=256, wtype="bf16",
+                     ntype="bf16", kvtype="i8", ctx=0, steps=max_ctx, seed=10)
+    st = DecodeStack(cfg, n_layers=1, attn_chunk=chunk)
+    std = 0.02 * np.sqrt(4096)
+    pre = synth.rand_cache((10, 1, max_ctx), nkv, max_ctx, d, "i8", std)
+    prv = synth.rand_cache((10, 2, max_ctx), nkv, max_ctx, d, "i8", std)
+    st.set_prefill(0, pre, prv)
+    codes_k, sc_k = pre.data.copy(), pre.scales.copy()
+    codes_v, sc_v = prv.data.copy(), prv.scales.copy()
+    for i, p in enumerate(positions):
+        q = synth.rand_f32((10, 3, i), (nq, d), std=std)
+        kn = synth.rand_f32((10, 4, i), (nkv, d), std=std)
+        vn = synth.rand_f32((10, 5, i), (nkv, d), std=std)
+        kn[0, :] = 0.0 if i == 1 else kn[0, :]            # a zero row once: scale 0, codes 0
+        st.q.copy_(torch.from_numpy(q.reshape(-1)))
+        st.Kstage[0].copy_(torch.from_numpy(kn))
+        st.Vstage[0].copy_(torch.from_numpy(vn))
+        st.set_pos(p)
+        L.dec_attn_splitk(st.desc, st.state[0])
+        torch.cuda.synchronize()
+        ck, sk = oracle.quantize_i8(kn)
+        cv, sv = oracle.quantize_i8(vn)
+        assert np.array_equal(st.K[0, :, p].cpu().numpy(), ck), f"key codes at {p}"
+        assert np.array_equal(st.V[0, :, p].cpu().numpy(), cv), f"value codes at {p}"
+        assert np.array_equal(st.Ks[0, :, p].cpu().numpy(), sk) and np.array_equal(st.Vs[0, :, p].cpu().numpy(), sv)
+        codes_k[:, p], sc_k[:, p], codes_v[:, p], sc_v[:, p] = ck, sk, cv, sv
+        Kd = oracle.ref.cache_values(codes_k[:, : p + 1], "i8", np.float64, sc_k[:, : p + 1])
+        Vd = oracle.ref.cache_values(codes_v[:, : p + 1], "i8", np.float64, sc_v[:, : p + 1])
+        ref = oracle.attend(q.astype(np.float64), Kd, Vd, nq // nkv)
+        assert rel_l2(st.attn.cpu().numpy(), ref.reshape(-1)) <= TOL, f"pos {p}"
+        assert int(st.counters.abs().sum().item()) == 0
+    assert st.check_err() == 0
+
+
 def test_combiner_give_up_sets_sync_error_and_recovers(gpu):
     """The attention combine's failure path, forced from the host:
     DEC_TEST_NO_WAIT makes every combiner but the last arrival of a kv head

@@ -31,6 +31,9 @@ int64_t pad4(int64_t n) { return (n + 3) / 4 * 4; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// the kernels' cache type: 0 f32, 1 bf16, 2 int8 rows with a scale each
+int kv_kind(const dec_layer_desc* d) { return d->kvtype == DEC_BF16 ? 1 : d->kvtype == DEC_I8 ? 2 : 0; }
+
 int ge_of(int wtype) { return wtype == DEC_F32 ? 4 : wtype == DEC_BF16 ? 8 : 32; }
 
 // The attention plan of a layer shape: the kernel DEC_ATTN_* in its flags
@@ -45,7 +48,7 @@ bool attn_plan_of(const dec_layer_desc* d, int* chunk, int* ns, int* nw, int* ki
     case DEC_ATTN_LOCAL: req = dec::kAttnLocal; break;
     default: break;
   }
-  return dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, d->kvtype == DEC_BF16 ? 1 : 0, d->max_ctx,
+  return dec::attn_plan(d->n_q_heads, d->n_kv_heads, d->head_dim, kv_kind(d), d->max_ctx,
                         d->attn_chunk, req, chunk, ns, nw, kind);
 }
 
@@ -53,8 +56,10 @@ int check_desc(const dec_layer_desc* d) {
   if (!d) return fail(DEC_E_NULL, "desc is NULL");
   if (d->wtype < DEC_F32 || d->wtype > DEC_Q4) return fail(DEC_E_DTYPE, "wtype %d", d->wtype);
   if (d->ntype != DEC_F32 && d->ntype != DEC_BF16) return fail(DEC_E_DTYPE, "ntype %d", d->ntype);
-  if (d->kvtype != DEC_F32 && d->kvtype != DEC_BF16) return fail(DEC_E_DTYPE, "kvtype %d", d->kvtype);
+  if (d->kvtype != DEC_F32 && d->kvtype != DEC_BF16 && d->kvtype != DEC_I8) return fail(DEC_E_DTYPE, "kvtype %d", d->kvtype);
   if (d->head_dim != 64 && d->head_dim != 128) return fail(DEC_E_SHAPE, "head_dim %d (64 or 128)", d->head_dim);
+  if (d->kvtype == DEC_I8 && d->head_dim != 128)
+    return fail(DEC_E_SHAPE, "int8 cache needs head_dim 128 (got %d)", d->head_dim);
   if (d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->n_q_heads % d->n_kv_heads)
     return fail(DEC_E_SHAPE, "heads %d/%d", d->n_q_heads, d->n_kv_heads);
   const int g = d->n_q_heads / d->n_kv_heads;
@@ -98,7 +103,7 @@ dec::GemvArgs base_args(const dec_layer_desc* d) {
   a.nkv = d->n_kv_heads;
   a.d = d->head_dim;
   a.max_ctx = d->max_ctx;
-  a.kvtype = d->kvtype == DEC_BF16 ? 1 : 0;
+  a.kvtype = kv_kind(d);
   a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
   a.fault = ((d->flags & DEC_TEST_SKIP_ROPE) ? dec::kFaultSkipRope : 0) |
             ((d->flags & DEC_TEST_APPEND_NEXT) ? dec::kFaultAppendNext : 0);
@@ -139,7 +144,7 @@ int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t 
   a.nkv = d->n_kv_heads;
   a.d = d->head_dim;
   a.max_ctx = d->max_ctx;
-  a.kvtype = d->kvtype == DEC_BF16 ? 1 : 0;
+  a.kvtype = kv_kind(d);
   a.null_kernel = (d->flags & DEC_NULL_KERNELS) ? 1 : 0;
   a.no_wait = (d->flags & DEC_TEST_NO_WAIT) ? 1 : 0;
   a.drop_last = (d->flags & DEC_TEST_DROP_SPLIT) ? 1 : 0;
@@ -151,7 +156,7 @@ int attn_launch(const dec_layer_desc* d, const dec_layer_state* st, hipStream_t 
 // The combine inside the output projection: bf16 weights and cache and a
 // split count it supports.
 bool attn_o_possible(const dec_layer_desc* d) {
-  if (d->wtype != DEC_BF16 || d->kvtype != DEC_BF16) return false;
+  if (d->wtype != DEC_BF16 || (d->kvtype != DEC_BF16 && d->kvtype != DEC_I8)) return false;
   int chunk, ns, nw, kind;
   attn_plan_of(d, &chunk, &ns, &nw, &kind);
   return dec::attn_o_supported(d->n_q_heads, d->n_kv_heads, d->head_dim, ns);
@@ -238,7 +243,7 @@ int qkv_unfused(const dec_layer_desc* d, const dec_layer_weights* w, const dec_l
   if ((rc = launched(gemv(d->wtype, dec::kEpiStore, a, s), "gemv_qkv"))) return rc;
   return launched(dec::launch_rope_append(y, st->q, st->k_cache, st->v_cache, st->pos, st->rope, st->err,
                                           d->n_q_heads, d->n_kv_heads, d->head_dim, d->max_ctx,
-                                          d->kvtype == DEC_BF16 ? 1 : 0, nullk, s),
+                                          kv_kind(d), nullk, s),
                   "rope_append");
 }
 
@@ -358,6 +363,24 @@ int64_t dec_attn_part_floats(const dec_layer_desc* d) {
   int chunk, ns, nw, kind;
   attn_plan_of(d, &chunk, &ns, &nw, &kind);
   return int64_t(d->n_q_heads) * ns * (d->head_dim + 2);
+}
+
+int64_t dec_cache_bytes(const dec_layer_desc* d) {
+  if (check_desc(d)) return -1;
+  if (d->kvtype == DEC_I8) return int64_t(dec::kv_i8_bytes(d->n_kv_heads, d->max_ctx, d->head_dim));
+  return int64_t(d->n_kv_heads) * d->max_ctx * d->head_dim * (d->kvtype == DEC_BF16 ? 2 : 4);
+}
+
+int64_t dec_cache_scale_offset(const dec_layer_desc* d) {
+  if (check_desc(d)) return -1;
+  if (d->kvtype != DEC_I8) return fail(DEC_E_DTYPE, "scales: the cache is not int8"), -1;
+  return int64_t(dec::kv_i8_scale_off(d->n_kv_heads, d->max_ctx, d->head_dim));
+}
+
+int64_t dec_cache_stage_offset(const dec_layer_desc* d) {
+  if (check_desc(d)) return -1;
+  if (d->kvtype != DEC_I8) return fail(DEC_E_DTYPE, "stage: the cache is not int8"), -1;
+  return int64_t(dec::kv_i8_stage_off(d->n_kv_heads, d->max_ctx, d->head_dim));
 }
 
 int64_t dec_scratch_floats(const dec_layer_desc* d) {

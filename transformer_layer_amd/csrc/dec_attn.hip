@@ -14,6 +14,15 @@
 // during the softmax. With a single row step the scores are too short to
 // cover V's latency, and V is requested right after K.
 //
+// An int8 cache (KVT 2) keeps one float scale per row: the score of a row is
+// its code dot product times the key row's scale, and its weight in p.v is
+// p times the value row's scale. The token's own row is not read from the
+// cache: the split that holds position p stops its loops one row short,
+// and its wave 0 quantizes the staged float k and v rows (one scale per row:
+// max |x| / 127; codes x * (127 / max |x|) rounded half to even, all in
+// float32), stores codes and scales into slot p, and scores and sums the
+// token from those codes.
+//
 // Partials, arrival and combine: attn_finish (dec_attn_common.h).
 #include "dec_attn_common.h"
 
@@ -23,7 +32,8 @@ template <int D, int KVT, int G, int NW, bool VLATE>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int kWaves = NW;        // waves per workgroup (4 or 8)
   constexpr int kBlock = NW * 64;
-  constexpr int EB = KVT == 1 ? 2 : 4;  // bytes per cache element
+  constexpr int EB = KVT == 1 ? 2 : KVT == 2 ? 1 : 4;  // bytes per cache element
+  constexpr bool I8 = KVT == 2;
   constexpr int DPL = 16 / EB;          // dims per lane
   constexpr int LPR = D / DPL;          // lanes per cache row
   constexpr int RPW = kWave / LPR;      // rows per wave load
@@ -45,7 +55,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int t0 = s * a.chunk;
   const int t1 = min(t0 + a.chunk, L);
   const int n = t1 - t0;
-  const int nsteps = (n + RPS - 1) / RPS;
+  // int8 cache: the split holding the token's position leaves that row to
+  // wave 0 (below); the loops read rows t0 .. tl-1 from the cache
+  const bool newrow = I8 && s == ns - 1;
+  const int tl = newrow ? t1 - 1 : t1;
+  const int nsteps = (tl - t0 + RPS - 1) / RPS;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
@@ -56,6 +70,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.vc) + size_t(j) * a.max_ctx * D * EB;
   const u32x4 z = {0u, 0u, 0u, 0u};
   auto row = [&](int step) { return t0 + step * RPS + wv * RPW + sub; };
+  // int8 cache: per-row scales of this kv head, and of each row step in flight
+  const size_t scale_off = I8 ? kv_i8_scale_off(a.nkv, a.max_ctx, D) : 0;
+  const float* ksc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.kc) + scale_off) +
+                     size_t(j) * a.max_ctx;
+  const float* vsc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.vc) + scale_off) +
+                     size_t(j) * a.max_ctx;
+  float ks[I8 ? U : 1], vs[I8 ? U : 1];
 
   // first batch of K rows, of V rows (VLATE: once the scores are done),
   // then the queries
@@ -64,15 +85,17 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = row(u);
-      const bool ok = u < nsteps && t < t1;
+      const bool ok = u < nsteps && t < tl;
       vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
+      if constexpr (I8) vs[u] = ok ? vsc[t] : 0.0f;
     }
   };
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int t = row(u);
-    const bool ok = u < nsteps && t < t1;
+    const bool ok = u < nsteps && t < tl;
     kv[u] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + d0) * EB) : z;
+    if constexpr (I8) ks[u] = ok ? ksc[t] : 0.0f;
   }
   if constexpr (!VLATE) first_v();
   const float qscale = kLog2e / sqrtf(float(D));
@@ -100,14 +123,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = row(b + u);
-        const bool ok = b + u < nsteps && t < t1;
+        const bool ok = b + u < nsteps && t < tl;
         kv[u] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + d0) * EB) : z;
+        if constexpr (I8) ks[u] = ok ? ksc[t] : 0.0f;
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = row(b + u);
-      const bool ok = b + u < nsteps && t < t1;
+      const bool ok = b + u < nsteps && t < tl;
       float kf[DPL];
       unpack_row<KVT>(kv[u], kf);
 #pragma unroll
@@ -116,8 +140,44 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < DPL; ++e) p = fmaf(qv[hh][e], kf[e], p);
         p = group_sum<LPR>(p);
+        if constexpr (I8) p *= ks[u];
         if (ok && li == 0) sc[hh][t - t0] = p;
       }
+    }
+  }
+  // int8 cache, the split holding the token: wave 0 quantizes the staged k
+  // and v rows (two dims a lane), appends them at slot pos and scores the
+  // token's row; its value codes wait in registers for the sum below
+  float nv0 = 0.0f, nv1 = 0.0f, nvs = 0.0f;
+  if constexpr (I8) {
+    static_assert(!I8 || D == 2 * kWave, "int8 cache rows: two dims a lane");
+    if (newrow && wv == 0) {
+      const size_t so = kv_i8_stage_off(a.nkv, a.max_ctx, D);
+      const float2 kx = *reinterpret_cast<const float2*>(
+          reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.kc) + so) + size_t(j) * D + 2 * lane);
+      const float2 vx = *reinterpret_cast<const float2*>(
+          reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.vc) + so) + size_t(j) * D + 2 * lane);
+      float kc0, kc1, kscale, vc0, vc1, vscale;
+      quantize_pair_i8(kx, kc0, kc1, kscale);
+      quantize_pair_i8(vx, vc0, vc1, vscale);
+      const size_t slot = size_t(j) * a.max_ctx + pos;
+      uint8_t* kcw = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.kc));
+      uint8_t* vcw = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.vc));
+      *reinterpret_cast<uint16_t*>(kcw + slot * D + 2 * lane) = pack_i8_pair(kc0, kc1);
+      *reinterpret_cast<uint16_t*>(vcw + slot * D + 2 * lane) = pack_i8_pair(vc0, vc1);
+      if (lane == 0) {
+        *reinterpret_cast<float*>(kcw + scale_off + slot * 4) = kscale;
+        *reinterpret_cast<float*>(vcw + scale_off + slot * 4) = vscale;
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float2 qx = *reinterpret_cast<const float2*>(a.q + (j * G + hh) * D + 2 * lane);
+        float d = wave_sum(fmaf(qx.x, kc0, qx.y * kc1));
+        if (lane == 0) sc[hh][n - 1] = d * kscale * qscale;
+      }
+      nv0 = vc0;
+      nv1 = vc1;
+      nvs = vscale;
     }
   }
   if constexpr (VLATE) first_v();
@@ -150,19 +210,20 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = row(b + u);
-        const bool ok = b + u < nsteps && t < t1;
+        const bool ok = b + u < nsteps && t < tl;
         vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
+        if constexpr (I8) vs[u] = ok ? vsc[t] : 0.0f;
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = row(b + u);
-      if (b + u < nsteps && t < t1) {
+      if (b + u < nsteps && t < tl) {
         float vf[DPL];
         unpack_row<KVT>(vv[u], vf);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          const float p = sc[hh][t - t0];
+          const float p = I8 ? sc[hh][t - t0] * vs[u] : sc[hh][t - t0];
 #pragma unroll
           for (int e = 0; e < DPL; ++e) o[hh][e] = fmaf(p, vf[e], o[hh][e]);
         }
@@ -179,6 +240,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
       for (int e = 0; e < DPL; ++e) ored[wv][hh][d0 + e] = o[hh][e];
+  if constexpr (I8) {
+    // the token's own value row (its score is now its weight in sc)
+    if (newrow && wv == 0)
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float p = sc[hh][n - 1] * nvs;
+        ored[0][hh][2 * lane] += p * nv0;
+        ored[0][hh][2 * lane + 1] += p * nv1;
+      }
+  }
   __syncthreads();
 
   attn_finish<D, G, NW>(a, j, s, ns, AttnShared{&ored[0][0][0], &stat[0][0], &cwts[0][0], cden, caccs, &role});
@@ -194,7 +265,7 @@ static int target_splits(int n_kv) {
 // over the whole cache, a multiple of 16 rows and no longer than one batch
 // of rows in flight
 static int batched_default_chunk(int n_kv, int head_dim, int kvtype, int max_ctx) {
-  const int lanes_per_row = head_dim * (kvtype == 1 ? 2 : 4) / 16;
+  const int lanes_per_row = head_dim * (kvtype == 1 ? 2 : kvtype == 2 ? 1 : 4) / 16;
   const int one_batch = (kWave / lanes_per_row) * 4 * 8;
   const int splits = target_splits(n_kv);
   int c = (max_ctx + splits - 1) / splits;
@@ -220,9 +291,12 @@ static int wide_default_chunk(int n_kv, int max_ctx, int cmax) {
 
 bool attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int kind_req, int* chunk,
                int* nsplit, int* waves, int* kind) {
-  const int smax = attn_lds_max_chunk(n_q, n_kv, head_dim, kvtype);   // streaming kernel: 0 if none fits
+  // an int8 cache runs on the batched kernel only (128-wide heads)
+  const bool i8 = kvtype == 2;
+  const int smax = i8 ? 0 : attn_lds_max_chunk(n_q, n_kv, head_dim, kvtype);   // streaming kernel: 0 if none fits
   const int lmax = kvtype == 1 ? attn_local_max_chunk(head_dim, kvtype) : 0;
   int k = kind_req;
+  if (i8 && k == kAttnDefault) k = kAttnBatched;
   if (k == kAttnDefault) {
     if (chunk_req > 0) {
       // a requested chunk: the streaming kernel when its values fit in LDS
@@ -258,6 +332,7 @@ bool attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chu
     ok = smax > 0 && c <= smax;
     w = kLdsWaves;
   } else {
+    ok = k == kAttnBatched && (!i8 || head_dim == 128);
     k = kAttnBatched;
     c = chunk_req > 0 ? chunk_req : batched_default_chunk(n_kv, head_dim, kvtype, max_ctx);
     const int cmin = (max_ctx + kSplitMax - 1) / kSplitMax;
@@ -306,6 +381,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (a.kind == kAttnStream) return launch_attn_lds(a, s);
   if (a.kind == kAttnLocal) return launch_attn_local(a, s);
   if (a.nsplit > kSplitMax || a.chunk > kChunkMax) return hipErrorInvalidValue;
+  if (a.kvtype == 2) return a.d == 128 && a.waves == 4 ? go_attn_vl<128, 2, 4>(a, s) : hipErrorInvalidValue;
   if (a.d == 64) return a.kvtype == 1 ? go_attn_waves<64, 1>(a, s) : go_attn_waves<64, 0>(a, s);
   if (a.d == 128) return a.kvtype == 1 ? go_attn_waves<128, 1>(a, s) : go_attn_waves<128, 0>(a, s);
   return hipErrorInvalidValue;

@@ -28,15 +28,40 @@ constexpr int kCombiners = 8;          // workgroups that combine one kv head's 
 constexpr unsigned kSpinMax = 1u << 14;  // polls of a waiting combiner before it gives up
 constexpr int kNotCombiner = -1, kGaveUp = -2;   // workgroup roles after arrival (else the combiner slot)
 
+// 16 bytes of a cache row as floats: 4 f32 (KVT 0), 8 bf16 (KVT 1) or 16
+// int8 codes (KVT 2, still to be multiplied by the row's scale)
 template <int KVT>
 __device__ __forceinline__ void unpack_row(u32x4 v, float* f) {
   if constexpr (KVT == 1) {
     f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
     f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+  } else if constexpr (KVT == 2) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) f[4 * k + b] = float(int8_t(uint8_t(w[k] >> (8 * b))));
   } else {
     f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
   }
+}
+
+// One int8 cache row held two elements a lane across a wave (a row of 128):
+// scale = max |x| / 127 and inv = 127 / max |x| (float32 divisions, rounded
+// to nearest: the compiler's default for HIP), codes x * inv rounded half to
+// even and clamped to [-127, 127]; a zero row gives scale 0, codes 0.
+__device__ __forceinline__ void quantize_pair_i8(float2 x, float& c0, float& c1, float& scale) {
+  const float m = wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
+  const float inv = m > 0.0f ? 127.0f / m : 0.0f;
+  scale = m > 0.0f ? m / 127.0f : 0.0f;
+  c0 = fminf(fmaxf(rintf(x.x * inv), -127.0f), 127.0f);
+  c1 = fminf(fmaxf(rintf(x.y * inv), -127.0f), 127.0f);
+}
+
+// two codes (integral floats in [-127, 127]) as the bytes of one 16-bit store
+__device__ __forceinline__ uint16_t pack_i8_pair(float c0, float c1) {
+  return uint16_t(uint8_t(int8_t(int(c0)))) | uint16_t(uint16_t(uint8_t(int8_t(int(c1)))) << 8);
 }
 
 // Two floats as one agent-scope atomic store (8-byte aligned address).

@@ -169,7 +169,12 @@ struct PairEpi {
         const int slot = (a.fault & kFaultAppendNext) && pos + 1 < a.max_ctx ? pos + 1 : pos;
         const size_t off = (size_t(j) * a.max_ctx + slot) * a.d + i;
         void* cache = isk ? a.kc : a.vc;
-        if (a.kvtype == 1) {
+        if (a.kvtype == 2) {   // int8 cache: the row is staged as float, the attention appends it
+          float* st = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(cache) +
+                                               kv_i8_stage_off(a.nkv, a.max_ctx, a.d)) + size_t(j) * a.d + i;
+          st[0] = y0;
+          st[half] = y1;
+        } else if (a.kvtype == 1) {
           uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
           c16[off] = f32_to_bf16(y0);
           c16[off + half] = f32_to_bf16(y1);

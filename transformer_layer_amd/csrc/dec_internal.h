@@ -17,6 +17,20 @@ constexpr int kCounterStride = 16;  // uint32 words between two kv heads' arriva
 constexpr int kFaultSkipRope = 0x1;    // q and k left unrotated
 constexpr int kFaultAppendNext = 0x2;  // k, v stored at position pos + 1 (pos itself when pos + 1 is past the cache)
 
+// Sections of an int8 cache allocation (256-byte aligned): codes
+// [nkv][max_ctx][d], one float scale per row [nkv][max_ctx], the newest row
+// [nkv][d] as float (the QKV step writes it, the attention appends it).
+__host__ __device__ constexpr size_t kv_align256(size_t n) { return (n + 255) / 256 * 256; }
+__host__ __device__ constexpr size_t kv_i8_scale_off(int nkv, int max_ctx, int d) {
+  return kv_align256(size_t(nkv) * max_ctx * d);
+}
+__host__ __device__ constexpr size_t kv_i8_stage_off(int nkv, int max_ctx, int d) {
+  return kv_align256(kv_i8_scale_off(nkv, max_ctx, d) + size_t(nkv) * max_ctx * 4);
+}
+__host__ __device__ constexpr size_t kv_i8_bytes(int nkv, int max_ctx, int d) {
+  return kv_i8_stage_off(nkv, max_ctx, d) + size_t(nkv) * d * 4;
+}
+
 // Arguments of the GEMV-core kernels (passed by value).
 struct GemvArgs {
   const void* W;       // first matrix (elements)
@@ -34,7 +48,7 @@ struct GemvArgs {
   float* y2;
   float* x;
   // QKV epilogue
-  int nq, nkv, d, max_ctx, kvtype;
+  int nq, nkv, d, max_ctx, kvtype;   // kvtype 0 f32, 1 bf16, 2 int8 (staged as float)
   const int32_t* pos;
   const float* rope;
   void* kc;
@@ -95,7 +109,7 @@ struct AttnArgs {
   float* out;          // [n_q d]
   const int32_t* pos;
   uint32_t* err;
-  int nq, nkv, d, max_ctx, chunk, nsplit, kvtype;
+  int nq, nkv, d, max_ctx, chunk, nsplit, kvtype;   // kvtype 0 f32, 1 bf16, 2 int8 rows + scales
   int waves;           // waves per workgroup (4 or 8)
   int kind;            // kAttnBatched, kAttnStream or kAttnLocal: which kernel runs
   int no_wait;         // combiners give up at once when splits are missing (failure-path tests)

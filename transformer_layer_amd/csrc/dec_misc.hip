@@ -100,7 +100,12 @@ __global__ void rope_append_kernel(const float* y, float* q, void* kc, void* vc,
   const int j = isk ? head - nq : head - nq - nkv;
   const size_t off = (size_t(j) * max_ctx + pos) * d + i;
   void* cache = isk ? kc : vc;
-  if (kvtype == 1) {
+  if (kvtype == 2) {   // int8 cache: the row is staged as float, the attention appends it
+    float* st = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(cache) + kv_i8_stage_off(nkv, max_ctx, d)) +
+                size_t(j) * d + i;
+    st[0] = y0;
+    st[half] = y1;
+  } else if (kvtype == 1) {
     uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
     c16[off] = f32_to_bf16(y0);
     c16[off + half] = f32_to_bf16(y1);

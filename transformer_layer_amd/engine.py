@@ -68,10 +68,24 @@ class DecodeStack:
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         self.rope = torch.empty(c.max_ctx * c.head_dim, dtype=f32, device=dev)
         L.dec_rope_table(float(c.rope_theta), c.head_dim, c.max_ctx, self.rope.data_ptr())
-        kvdt = f32 if c.kvtype == "f32" else torch.int16
         shape = (self.n_layers, c.n_kv_heads, c.max_ctx, c.head_dim)
-        self.K = torch.zeros(shape, dtype=kvdt, device=dev)
-        self.V = torch.zeros(shape, dtype=kvdt, device=dev)
+        if c.kvtype == "i8":
+            # per layer: int8 codes, one float scale per row, the staged newest row
+            nb = L.dec_cache_bytes(self.desc)
+            so, go = L.dec_cache_scale_offset(self.desc), L.dec_cache_stage_offset(self.desc)
+            ncode = c.n_kv_heads * c.max_ctx * c.head_dim
+            nrow = c.n_kv_heads * c.max_ctx
+            self.Kraw = torch.zeros((self.n_layers, nb), dtype=torch.uint8, device=dev)
+            self.Vraw = torch.zeros((self.n_layers, nb), dtype=torch.uint8, device=dev)
+            self.K, self.V = (r[:, :ncode].view(torch.int8).view(shape) for r in (self.Kraw, self.Vraw))
+            self.Ks, self.Vs = (r[:, so: so + 4 * nrow].view(torch.float32).view(shape[:3])
+                                for r in (self.Kraw, self.Vraw))
+            self.Kstage, self.Vstage = (r[:, go: go + 4 * c.n_kv_heads * c.head_dim].view(torch.float32)
+                                        .view(self.n_layers, c.n_kv_heads, c.head_dim) for r in (self.Kraw, self.Vraw))
+        else:
+            kvdt = f32 if c.kvtype == "f32" else torch.int16
+            self.K = torch.zeros(shape, dtype=kvdt, device=dev)
+            self.V = torch.zeros(shape, dtype=kvdt, device=dev)
         self.w = [None] * self.n_layers
         self.wstruct = [None] * self.n_layers
         self.state = [self._state(l) for l in range(self.n_layers)]
@@ -84,7 +98,9 @@ class DecodeStack:
         p = L.ptr
         return L.dec_layer_state(
             x=p(self.x), q=p(self.q), attn=p(self.attn), h=p(self.h), part=p(self.part),
-            counters=p(self.counters), k_cache=p(self.K[l]), v_cache=p(self.V[l]), pos=p(self.pos),
+            counters=p(self.counters),
+            k_cache=p(self.Kraw[l] if self.cfg.kvtype == "i8" else self.K[l]),
+            v_cache=p(self.Vraw[l] if self.cfg.kvtype == "i8" else self.V[l]), pos=p(self.pos),
             rope=p(self.rope), err=p(self.err), scratch=p(self.scratch))
 
     # ---- loading inputs
@@ -98,6 +114,11 @@ class DecodeStack:
 
     def set_prefill(self, l: int, K, V) -> None:
         n = K.data.shape[1]
+        if K.kind == "i8":
+            for st, codes, scales in ((K, self.K, self.Ks), (V, self.V, self.Vs)):
+                codes[l, :, :n] = torch.from_numpy(np.ascontiguousarray(st.data, dtype=np.int8)).to(self.dev)
+                scales[l, :, :n] = torch.from_numpy(np.ascontiguousarray(st.scales, dtype=np.float32)).to(self.dev)
+            return
         self.K[l, :, :n] = _upload(K, self.dev)[0]
         self.V[l, :, :n] = _upload(V, self.dev)[0]
 

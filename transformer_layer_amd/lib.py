@@ -12,8 +12,8 @@ import os
 
 LIBPATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libdec.so")
 
-DEC_F32, DEC_BF16, DEC_Q4 = 0, 1, 2
-DTYPES = {"f32": DEC_F32, "bf16": DEC_BF16, "q4": DEC_Q4}
+DEC_F32, DEC_BF16, DEC_Q4, DEC_I8 = 0, 1, 2, 3
+DTYPES = {"f32": DEC_F32, "bf16": DEC_BF16, "q4": DEC_Q4, "i8": DEC_I8}
 DEC_UNFUSED = 0x1
 DEC_NULL_KERNELS = 0x2
 DEC_NO_FUSE_QKV = 0x4
@@ -31,7 +31,7 @@ DEC_TEST_DROP_SPLIT = 0x800
 DEC_ERR_POS = 0x1
 DEC_ERR_TOKEN = 0x2
 DEC_ERR_SYNC = 0x4
-ABI_VERSION = 4
+ABI_VERSION = 5
 DEC_COUNTER_STRIDE = 16
 DEC_STATIC_SCRATCH_BYTES = 4 << 20
 
@@ -70,6 +70,9 @@ P_ST = ctypes.POINTER(dec_layer_state)
 SIGNATURES = {
     "dec_attn_part_floats": (c_int64, [P_DESC]),
     "dec_scratch_floats": (c_int64, [P_DESC]),
+    "dec_cache_bytes": (c_int64, [P_DESC]),
+    "dec_cache_scale_offset": (c_int64, [P_DESC]),
+    "dec_cache_stage_offset": (c_int64, [P_DESC]),
     "dec_rmsnorm_gemv_qkv_rope": (ctypes.c_int, [P_DESC, P_W, P_ST, c_void_p]),
     "dec_attn_splitk": (ctypes.c_int, [P_DESC, P_ST, c_void_p]),
     "dec_attn_partials": (ctypes.c_int, [P_DESC, P_ST, c_void_p]),
@@ -146,6 +149,25 @@ def dec_scratch_floats(desc: dec_layer_desc) -> int:
     if n < 0:
         raise DecError(_lib.dec_last_error().decode())
     return n
+
+
+def _size(name: str, desc: dec_layer_desc) -> int:
+    n = getattr(load(), name)(ctypes.byref(desc))
+    if n < 0:
+        raise DecError(_lib.dec_last_error().decode())
+    return n
+
+
+def dec_cache_bytes(desc: dec_layer_desc) -> int:
+    return _size("dec_cache_bytes", desc)
+
+
+def dec_cache_scale_offset(desc: dec_layer_desc) -> int:
+    return _size("dec_cache_scale_offset", desc)
+
+
+def dec_cache_stage_offset(desc: dec_layer_desc) -> int:
+    return _size("dec_cache_stage_offset", desc)
 
 
 def dec_rmsnorm_gemv_qkv_rope(desc, weights, state, stream=None) -> None:
