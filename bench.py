@@ -310,11 +310,26 @@ class Workload:
         torch.cuda.empty_cache()
 
 
-def other_workload(name: str, steps: int, warmup: int, repeats: int) -> dict:
+def workload_config(spec: str):
+    """A workload by name, optionally over another KV cache type or cached
+    length: "C5", "C5:i8" (the same stack over an int8 cache), "C5@32768"
+    (32768 cached positions), "C5:i8@32768"."""
+    import synth
+    spec, _, ctx = spec.partition("@")
+    name, _, kv = spec.partition(":")
+    cfg = synth.CONFIGS[name]
+    if kv and kv != cfg.kvtype:
+        cfg = cfg.with_(kvtype=kv, name=f"{cfg.name}_{kv}kv")
+    if ctx and int(ctx) != cfg.ctx:
+        cfg = cfg.with_(ctx=int(ctx), name=f"{cfg.name}_ctx{int(ctx)}")
+    return cfg
+
+
+def other_workload(spec: str, steps: int, warmup: int, repeats: int) -> dict:
     """tok/s of another workload's stack: the median of `repeats` timed runs
     of `steps` tokens (same protocol as the headline)."""
-    import synth
-    cfg = synth.CONFIGS[name]
+    cfg = workload_config(spec)
+    name = spec.partition("@")[0].partition(":")[0]
     log(f"config {cfg.name}: building stack ({cfg.n_layers} layers)")
     w = Workload(cfg)
     runs = []
@@ -328,7 +343,8 @@ def other_workload(name: str, steps: int, warmup: int, repeats: int) -> dict:
     gbs = bpt * tok_s / 1e9
     out = {"tok_s": round(tok_s, 2), "tok_s_runs": [round(v, 2) for v in runs], "ms_per_step": round(1e3 / tok_s, 4),
            "bytes_per_token": int(bpt), "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-           "layers": cfg.n_layers, "weights": cfg.wtype, "context": cfg.ctx, "device_error": err}
+           "layers": cfg.n_layers, "weights": cfg.wtype, "kv_cache": cfg.kvtype, "context": cfg.ctx,
+           "device_error": err}
     if name in ("C3", "C4", "C5"):
         out["target_70pct_tok_s"] = round(0.7 * PEAK_HBM_GBS * 1e9 / bpt, 1)
     log(f"{cfg.name}: {tok_s:.1f} tok/s, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.3f} of peak)")
@@ -367,7 +383,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--config", default="C4")
+    ap.add_argument("--config", default="C4",
+                    help="workload: NAME, NAME:i8 (over an int8 KV cache), NAME@CTX (CTX cached positions)")
     ap.add_argument("--unfused", action="store_true")
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--null-kernels", action="store_true")
@@ -376,8 +393,9 @@ def main() -> int:
     ap.add_argument("--no-head", action="store_true", help="skip the greedy (LM head) timing")
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed runs of --steps tokens for the median (the first is the headline value)")
-    ap.add_argument("--others", default="C3,C5,C2",
-                    help="other workloads timed the same way and reported under `workloads` ('' for none)")
+    ap.add_argument("--others", default="C3,C5,C2,C4:i8,C5:i8",
+                    help="other workloads timed the same way and reported under `workloads` ('' for none); "
+                         "NAME:i8 is NAME over an int8 KV cache")
     ap.add_argument("--ab", action="store_true",
                     help="only the paired A/B modes (graph/eager, fused/unfused, null kernels) on --config")
     ap.add_argument("--ffn-reps", type=int, default=4,
@@ -394,7 +412,7 @@ def main() -> int:
     import synth
     from transformer_layer_amd import lib as L
 
-    cfg = synth.CONFIGS[args.config]
+    cfg = workload_config(args.config)
     if args.ab:
         res = ab_modes(cfg, args.steps, args.warmup)
         print(json.dumps({"config": cfg.name, "steps": args.steps, "ab": res}), flush=True)
@@ -444,8 +462,8 @@ def main() -> int:
 
     others = {}
     if not args.null_kernels and not args.unfused and not args.eager:
-        for name in [n for n in args.others.split(",") if n and n != args.config]:
-            others[synth.CONFIGS[name].name] = other_workload(name, args.steps, args.warmup, 3)
+        for spec in [n for n in args.others.split(",") if n and n != args.config]:
+            others[workload_config(spec).name] = other_workload(spec, args.steps, args.warmup, 3)
 
     cpu = None
     if not args.no_cpu:
