@@ -16,12 +16,14 @@
 //
 // An int8 cache (KVT 2) keeps one float scale per row: the score of a row is
 // its code dot product times the key row's scale, and its weight in p.v is
-// p times the value row's scale. The token's own row is not read from the
-// cache: the split that holds position p stops its loops one row short,
-// and its wave 0 quantizes the staged float k and v rows (one scale per row:
-// max |x| / 127; codes x * (127 / max |x|) rounded half to even, all in
-// float32), stores codes and scales into slot p, and scores and sums the
-// token from those codes.
+// p times the value row's scale. Each lane loads the scales of its rows of
+// the softmax pass (t0 + lane + 64 k) once at launch, and the softmax pass
+// applies them: the row loops read codes only. The token's own row is not
+// read from the cache: the split that holds position p stops its loops one
+// row short, and its wave 0 (which requests the staged float k and v rows at
+// launch) quantizes them (one scale per row: max |x| / 127; codes
+// x * (127 / max |x|) rounded half to even, all in float32), stores codes and
+// scales into slot p, and scores and sums the token from those codes.
 //
 // Partials, arrival and combine: attn_finish (dec_attn_common.h).
 #include "dec_attn_common.h"
@@ -70,13 +72,33 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.vc) + size_t(j) * a.max_ctx * D * EB;
   const u32x4 z = {0u, 0u, 0u, 0u};
   auto row = [&](int step) { return t0 + step * RPS + wv * RPW + sub; };
-  // int8 cache: per-row scales of this kv head, and of each row step in flight
+  // int8 cache: the scales of this lane's softmax rows (t0 + lane + 64 k;
+  // the index is clamped into the cache rows read, the values past them are
+  // never used), and wave 0 of the token's split requests the staged rows
+  constexpr int KS = I8 ? kChunkMax / kWave : 1;
   const size_t scale_off = I8 ? kv_i8_scale_off(a.nkv, a.max_ctx, D) : 0;
-  const float* ksc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.kc) + scale_off) +
-                     size_t(j) * a.max_ctx;
-  const float* vsc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.vc) + scale_off) +
-                     size_t(j) * a.max_ctx;
-  float ks[I8 ? U : 1], vs[I8 ? U : 1];
+  float rks[KS], rvs[KS];
+  float2 kx = {0.0f, 0.0f}, vx = {0.0f, 0.0f};
+  if constexpr (I8) {
+    const float* ksc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.kc) + scale_off) +
+                       size_t(j) * a.max_ctx;
+    const float* vsc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.vc) + scale_off) +
+                       size_t(j) * a.max_ctx;
+    const int tmax = tl > t0 ? tl - 1 : t0;   // t0 <= pos < max_ctx
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const int t = min(t0 + lane + k * kWave, tmax);
+      rks[k] = ksc[t];
+      rvs[k] = vsc[t];
+    }
+    if (newrow && wv == 0) {
+      const size_t so = kv_i8_stage_off(a.nkv, a.max_ctx, D);
+      kx = *reinterpret_cast<const float2*>(
+          reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.kc) + so) + size_t(j) * D + 2 * lane);
+      vx = *reinterpret_cast<const float2*>(
+          reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.vc) + so) + size_t(j) * D + 2 * lane);
+    }
+  }
 
   // first batch of K rows, of V rows (VLATE: once the scores are done),
   // then the queries
@@ -87,7 +109,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       const int t = row(u);
       const bool ok = u < nsteps && t < tl;
       vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
-      if constexpr (I8) vs[u] = ok ? vsc[t] : 0.0f;
     }
   };
 #pragma unroll
@@ -95,7 +116,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     const int t = row(u);
     const bool ok = u < nsteps && t < tl;
     kv[u] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + d0) * EB) : z;
-    if constexpr (I8) ks[u] = ok ? ksc[t] : 0.0f;
   }
   if constexpr (!VLATE) first_v();
   const float qscale = kLog2e / sqrtf(float(D));
@@ -125,7 +145,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         const int t = row(b + u);
         const bool ok = b + u < nsteps && t < tl;
         kv[u] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + d0) * EB) : z;
-        if constexpr (I8) ks[u] = ok ? ksc[t] : 0.0f;
       }
     }
 #pragma unroll
@@ -140,7 +159,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < DPL; ++e) p = fmaf(qv[hh][e], kf[e], p);
         p = group_sum<LPR>(p);
-        if constexpr (I8) p *= ks[u];
         if (ok && li == 0) sc[hh][t - t0] = p;
       }
     }
@@ -152,11 +170,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   if constexpr (I8) {
     static_assert(!I8 || D == 2 * kWave, "int8 cache rows: two dims a lane");
     if (newrow && wv == 0) {
-      const size_t so = kv_i8_stage_off(a.nkv, a.max_ctx, D);
-      const float2 kx = *reinterpret_cast<const float2*>(
-          reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.kc) + so) + size_t(j) * D + 2 * lane);
-      const float2 vx = *reinterpret_cast<const float2*>(
-          reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.vc) + so) + size_t(j) * D + 2 * lane);
       float kc0, kc1, kscale, vc0, vc1, vscale;
       quantize_pair_i8(kx, kc0, kc1, kscale);
       quantize_pair_i8(vx, vc0, vc1, vscale);
@@ -183,19 +196,46 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   if constexpr (VLATE) first_v();
   __syncthreads();
 
-  // ---- per head: m = max s, p = exp2(s - m), l = sum p (one exponential per entry)
+  // ---- per head: m = max s, p = exp2(s - m), l = sum p (one exponential per
+  // entry); an int8 cache's row scales enter here: s = the code score times
+  // the key scale, and the PV loop reads p times the value scale (the
+  // token's row, already scaled, keeps factor 1)
   for (int hh = wv; hh < G; hh += kWaves) {
     float m = -INFINITY;
-    for (int i = lane; i < n; i += kWave) m = fmaxf(m, sc[hh][i]);
-    m = wave_max(m);
-    float l = 0.0f;
-    for (int i = lane; i < n; i += kWave) {
-      const float p = exp2f(sc[hh][i] - m);
-      sc[hh][i] = p;
-      l += p;
+    if constexpr (I8) {
+      const int nc = tl - t0;   // rows read from the cache
+      float sv[KS];
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const int i = lane + k * kWave;
+        sv[k] = i < n ? sc[hh][i] * (i < nc ? rks[k] : 1.0f) : -INFINITY;
+        m = fmaxf(m, sv[k]);
+      }
+      m = wave_max(m);
+      float l = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const int i = lane + k * kWave;
+        if (i < n) {
+          const float p = exp2f(sv[k] - m);
+          sc[hh][i] = i < nc ? p * rvs[k] : p;
+          l += p;
+        }
+      }
+      l = wave_sum(l);
+      if (lane == 0) { stat[hh][0] = m; stat[hh][1] = l; }
+    } else {
+      for (int i = lane; i < n; i += kWave) m = fmaxf(m, sc[hh][i]);
+      m = wave_max(m);
+      float l = 0.0f;
+      for (int i = lane; i < n; i += kWave) {
+        const float p = exp2f(sc[hh][i] - m);
+        sc[hh][i] = p;
+        l += p;
+      }
+      l = wave_sum(l);
+      if (lane == 0) { stat[hh][0] = m; stat[hh][1] = l; }
     }
-    l = wave_sum(l);
-    if (lane == 0) { stat[hh][0] = m; stat[hh][1] = l; }
   }
   __syncthreads();
 
@@ -212,7 +252,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         const int t = row(b + u);
         const bool ok = b + u < nsteps && t < tl;
         vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
-        if constexpr (I8) vs[u] = ok ? vsc[t] : 0.0f;
       }
     }
 #pragma unroll
@@ -223,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         unpack_row<KVT>(vv[u], vf);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          const float p = I8 ? sc[hh][t - t0] * vs[u] : sc[hh][t - t0];
+          const float p = sc[hh][t - t0];
 #pragma unroll
           for (int e = 0; e < DPL; ++e) o[hh][e] = fmaf(p, vf[e], o[hh][e]);
         }
