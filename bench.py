@@ -388,6 +388,8 @@ def main() -> int:
     ap.add_argument("--unfused", action="store_true")
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--null-kernels", action="store_true")
+    ap.add_argument("--fuse-down", action="store_true",
+                    help="4-bit weights: the gated FFN and the down projection as one kernel (four per layer)")
     ap.add_argument("--attn-chunk", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip the greedy (LM head) timing")
@@ -417,7 +419,8 @@ def main() -> int:
         res = ab_modes(cfg, args.steps, args.warmup)
         print(json.dumps({"config": cfg.name, "steps": args.steps, "ab": res}), flush=True)
         return 0
-    flags = (L.DEC_UNFUSED if args.unfused else 0) | (L.DEC_NULL_KERNELS if args.null_kernels else 0)
+    flags = ((L.DEC_UNFUSED if args.unfused else 0) | (L.DEC_NULL_KERNELS if args.null_kernels else 0)
+             | (L.DEC_FUSE_DOWN if args.fuse_down else 0))
     log(f"config {cfg.name}: building stack ({cfg.n_layers} layers)")
     w = Workload(cfg, flags, args.attn_chunk, eager=args.eager)
     st = w.st
@@ -488,9 +491,9 @@ def main() -> int:
                    "heads_q_kv": [cfg.n_q_heads, cfg.n_kv_heads], "head_dim": cfg.head_dim,
                    "ffn": cfg.ffn, "weights": cfg.wtype, "kv_cache": cfg.kvtype,
                    "context": cfg.ctx, "decode_window": cfg.steps, "batch": 1,
-                   "mode": ("unfused" if args.unfused else "fused") + ("-eager" if args.eager else "-graph")
-                           + ("-null" if args.null_kernels else ""),
-                   "kernels_per_layer": 10 if args.unfused else 5},
+                   "mode": ("unfused" if args.unfused else "fused") + ("-down" if args.fuse_down else "")
+                           + ("-eager" if args.eager else "-graph") + ("-null" if args.null_kernels else ""),
+                   "kernels_per_layer": 10 if args.unfused else 4 if args.fuse_down else 5},
         "bytes_per_token": int(bpt),
         "hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define DEC_ABI_VERSION 5
+#define DEC_ABI_VERSION 6
 
 enum dec_dtype { DEC_F32 = 0, DEC_BF16 = 1, DEC_Q4 = 2, DEC_I8 = 3 };
 
@@ -73,14 +73,17 @@ enum dec_status {
 
 /* uint32 words per kv head in dec_layer_state.counters: kv head j uses words
    j * DEC_COUNTER_STRIDE (+0 arrivals, +1 finished combiners), alone on
-   their 64-byte line */
+   their 64-byte line; words 2 and 3 of the first line count the grid-wide
+   arrivals and departures of dec_gated_ffn_down */
 #define DEC_COUNTER_STRIDE 16
 
 /* bits of the device error word */
 #define DEC_ERR_POS 0x1u
 #define DEC_ERR_TOKEN 0x2u
 #define DEC_ERR_SYNC 0x4u  /* an attention combiner stopped waiting for the other
-                              splits of its kv head; that output slice is not written */
+                              splits of its kv head (that output slice is not
+                              written), or a dec_gated_ffn_down workgroup stopped
+                              waiting for the others (its 16 rows of x not updated) */
 
 /* dec_layer_desc.flags.
    Fusion controls, global and per fused operation ("backend-specific kernel
@@ -97,6 +100,9 @@ enum dec_status {
                                     projection is a plain dec_gemv_residual */
 #define DEC_DETERMINISTIC 0x20u /* no float atomics on the path, so repeated runs give the
                                    same bits (takes the DEC_NO_FUSE_ATTN_O path) */
+#define DEC_FUSE_DOWN 0x40u     /* 4-bit weights: the gated FFN and the down projection as one
+                                   kernel (dec_gated_ffn_down), four kernels per layer; ignored
+                                   with DEC_UNFUSED or DEC_NO_FUSE_FFN */
 
 /* Which attention kernel runs (a two-bit field; 0 = the library's choice
    for the shape). All three compute the same split-K reduction ("RDNA4
@@ -282,6 +288,26 @@ int dec_gemv_residual(const dec_layer_desc* desc, dec_mat w, int32_t rows, int32
 int dec_gated_ffn(const dec_layer_desc* desc, const void* ffn_norm, dec_mat wgate, dec_mat wup,
                   const float* x, float* h, void* stream);
 
+/* The gated FFN and the down projection with the residual add, in one
+   launch: x += wdown . h, h as dec_gated_ffn computes it from x ("RDNA4
+   Decode Kernel Fusion: Pipeline Barriers, Not Launches, Are the Win",
+   section "Fusion removes the barrier by removing the write": the figure's
+   four-kernel layer folds the down projection into the FFN). 4-bit weights
+   only (others: DEC_E_UNSUPPORTED). Reads w->ffn_norm, w->wgate, w->wup,
+   w->wdown and st->x; writes st->h (float32 [F]) and st->x; uses words 2
+   and 3 of st->counters (zero before the first call; every call leaves
+   them zero) and st->err. One workgroup per 16 rows of x; every workgroup
+   computes its share of h, then waits at a grid-wide counter until all
+   have, so all of them must be resident on the GPU at once: a shape whose
+   workgroups would not all fit on the current device, or whose rows exceed
+   the kernel's plans, returns DEC_E_SHAPE. A wait that does not
+   end within its bound sets DEC_ERR_SYNC and leaves that workgroup's rows
+   of x unchanged. h differs from dec_gated_ffn's in the last bits (its
+   sums are split over eight waves instead of four); x is within float32
+   rounding of dec_gated_ffn followed by dec_gemv_residual. */
+int dec_gated_ffn_down(const dec_layer_desc* desc, const dec_layer_weights* w, const dec_layer_state* st,
+                       void* stream);
+
 /* One whole decoder layer for the token at position *pos, in the order
    "RDNA4 Decode Kernel Fusion: Pipeline Barriers, Not Launches, Are the Win"
    gives in section "Decode is where the bubble has nowhere to go" (norm,
@@ -304,7 +330,8 @@ int dec_gated_ffn(const dec_layer_desc* desc, const void* ffn_norm, dec_mat wgat
    projection + residual, rmsnorm with multiply, gate/up projection,
    SwiGLU, down projection + residual), whose f32 and 4-bit results equal
    the fused ones bit for bit. st->scratch is needed when DEC_UNFUSED,
-   DEC_NO_FUSE_QKV or DEC_NO_FUSE_FFN is set. */
+   DEC_NO_FUSE_QKV or DEC_NO_FUSE_FFN is set. DEC_FUSE_DOWN (4-bit
+   weights) runs dec_gated_ffn_down in place of the last two kernels. */
 int dec_layer_step(const dec_layer_desc* desc, const dec_layer_weights* w,
                    const dec_layer_state* st, void* stream);
 

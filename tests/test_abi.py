@@ -90,6 +90,7 @@ int main(void) {
          DEC_NO_FUSE_FFN, DEC_NO_FUSE_ATTN_O);
   printf("DEC_DETERMINISTIC value %u\nDEC_TEST_SKIP_ROPE value %u\nDEC_TEST_APPEND_NEXT value %u\n",
          DEC_DETERMINISTIC, DEC_TEST_SKIP_ROPE, DEC_TEST_APPEND_NEXT);
+  printf("DEC_FUSE_DOWN value %u\n", DEC_FUSE_DOWN);
   printf("DEC_TEST_DROP_SPLIT value %u\nDEC_E_UNSUPPORTED value %d\n", DEC_TEST_DROP_SPLIT, DEC_E_UNSUPPORTED);
   printf("DEC_ERR_POS value %u\nDEC_ERR_TOKEN value %u\nDEC_ERR_SYNC value %u\n", DEC_ERR_POS, DEC_ERR_TOKEN,
          DEC_ERR_SYNC);
@@ -119,6 +120,7 @@ def test_struct_layout_matches_a_c_compiler(L, tmp_path):
                     "DEC_TEST_NO_WAIT": L.DEC_TEST_NO_WAIT, "DEC_NO_FUSE_QKV": L.DEC_NO_FUSE_QKV,
                     "DEC_NO_FUSE_FFN": L.DEC_NO_FUSE_FFN, "DEC_NO_FUSE_ATTN_O": L.DEC_NO_FUSE_ATTN_O,
                     "DEC_DETERMINISTIC": L.DEC_DETERMINISTIC, "DEC_TEST_SKIP_ROPE": L.DEC_TEST_SKIP_ROPE,
+                    "DEC_FUSE_DOWN": L.DEC_FUSE_DOWN,
                     "DEC_TEST_APPEND_NEXT": L.DEC_TEST_APPEND_NEXT, "DEC_TEST_DROP_SPLIT": L.DEC_TEST_DROP_SPLIT,
                     "DEC_E_UNSUPPORTED": E_UNSUPPORTED,
                     "DEC_ERR_POS": L.DEC_ERR_POS, "DEC_ERR_TOKEN": L.DEC_ERR_TOKEN, "DEC_ERR_SYNC": L.DEC_ERR_SYNC,
@@ -130,7 +132,7 @@ def test_struct_layout_matches_a_c_compiler(L, tmp_path):
         else:
             assert getattr(getattr(L, name), field).offset == val, f"{name}.{field}"
         seen += 1
-    assert seen == 60   # 4 sizes, 33 offsets, 23 constants
+    assert seen == 61   # 4 sizes, 33 offsets, 24 constants
 
 
 # ---- host-side checks (every call below is rejected before any launch)
@@ -254,6 +256,31 @@ def test_int8_cache_layout_and_shapes(L):
     assert rc_step(L, d, weights_of(L), state_of(L)) == E_SHAPE
     assert "int8 cache needs head_dim 128" in L.dec_last_error()
     assert L.load().dec_cache_bytes(ctypes.byref(d)) == -1
+
+
+def test_gated_ffn_down_refusals(L):
+    """The FFN with the down projection folded in runs 4-bit weights only,
+    and only shapes whose workgroups (one per 16 rows of x) can all be
+    resident at once and whose rows fit its plans; each refusal is made on
+    the host, before any launch."""
+    lib = L.load()
+    w, s = weights_of(L), state_of(L)
+
+    def call(d):
+        return lib.dec_gated_ffn_down(ctypes.byref(d), ctypes.byref(w), ctypes.byref(s), None)
+
+    bf = desc_of(L, synth.CONFIGS["C4"])
+    assert call(bf) == E_UNSUPPORTED and "4-bit" in L.dec_last_error()
+    bf.flags = L.DEC_FUSE_DOWN
+    assert rc_step(L, bf, w, s) == E_UNSUPPORTED
+    big = desc_of(L, synth.CONFIGS["C5"], hidden=8192)           # 512 workgroups of 155 VGPRs a lane
+    assert call(big) == E_SHAPE and "resident" in L.dec_last_error()
+    big.flags = L.DEC_FUSE_DOWN
+    assert rc_step(L, big, w, s) == E_SHAPE
+    noplan = desc_of(L, synth.CONFIGS["C5"], hidden=512, ffn=16384)   # 64 gate/up tiles per workgroup
+    assert call(noplan) == E_SHAPE and "no plan" in L.dec_last_error()
+    assert lib.dec_gated_ffn_down(ctypes.byref(desc_of(L, synth.CONFIGS["C5"])), None, ctypes.byref(s),
+                                  None) == E_NULL
 
 
 def test_null_arguments_are_rejected(L):

@@ -218,6 +218,58 @@ int ffn_launch(const dec_layer_desc* d, const void* norm, dec_mat wg, dec_mat wu
   return launched(gemv(d->wtype, dec::kEpiSwiglu, a, s), "gated_ffn");
 }
 
+// The gated FFN and the down projection in one launch (4-bit weights).
+void ffn_down_args(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st,
+                   dec::GemvArgs* f, dec::GemvArgs* dn) {
+  *f = base_args(d);
+  f->W = w->wgate.w;
+  f->S = w->wgate.scales;
+  f->W2 = w->wup.w;
+  f->S2 = w->wup.scales;
+  f->rows = d->ffn;
+  f->cols = d->hidden;
+  f->ntask = d->ffn;
+  f->in = st->x;
+  f->norm = w->ffn_norm;
+  f->y = st->h;
+  f->err = st->err;
+  *dn = base_args(d);
+  dn->W = w->wdown.w;
+  dn->S = w->wdown.scales;
+  dn->rows = d->hidden;
+  dn->cols = d->ffn;
+  dn->ntask = (d->hidden + 1) / 2;
+  dn->in = st->h;
+  dn->x = st->x;
+  dn->err = st->err;
+}
+
+// DEC_OK if the fused FFN + down kernel runs this shape on the current device.
+int ffn_down_possible(const dec_layer_desc* d) {
+  if (d->wtype != DEC_Q4) return fail(DEC_E_UNSUPPORTED, "the gated FFN with down folded in needs 4-bit weights");
+  dec_layer_weights w;
+  dec_layer_state st;
+  memset(&w, 0, sizeof w);
+  memset(&st, 0, sizeof st);
+  dec::GemvArgs f, dn;
+  ffn_down_args(d, &w, &st, &f, &dn);
+  const hipError_t e = dec::ffn_down_q4_check(f, dn);
+  if (e == hipErrorInvalidConfiguration)
+    return fail(DEC_E_SHAPE, "gated FFN + down: %d workgroups would not all be resident at once",
+                (d->hidden + 15) / 16);
+  if (e != hipSuccess) return fail(DEC_E_SHAPE, "gated FFN + down: no plan for hidden %d, ffn %d", d->hidden, d->ffn);
+  return DEC_OK;
+}
+
+int ffn_down_launch(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st,
+                    hipStream_t s) {
+  dec::GemvArgs f, dn;
+  ffn_down_args(d, w, st, &f, &dn);
+  const int no_wait = (d->flags & DEC_TEST_NO_WAIT) ? 1 : 0;
+  return launched(dec::launch_ffn_down_q4(f, dn, st->counters + dec::kFfnDownBarWord, no_wait, s),
+                  "gated_ffn_down");
+}
+
 // The first fused kernel as its four per-op kernels (rmsnorm, weight
 // multiply, QKV projection, RoPE + append), through `scratch`.
 int qkv_unfused(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st, hipStream_t s) {
@@ -447,13 +499,28 @@ int dec_gated_ffn(const dec_layer_desc* d, const void* ffn_norm, dec_mat wgate, 
   return ffn_launch(d, ffn_norm, wgate, wup, x, h, hipStream_t(stream));
 }
 
+int dec_gated_ffn_down(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st,
+                       void* stream) {
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_state(st, false))) return rc;
+  if (!w) return fail(DEC_E_NULL, "weights are NULL");
+  if (!w->ffn_norm) return fail(DEC_E_NULL, "ffn_norm is NULL");
+  if ((rc = check_mat(d, w->wgate, "wgate")) || (rc = check_mat(d, w->wup, "wup")) ||
+      (rc = check_mat(d, w->wdown, "wdown")))
+    return rc;
+  if ((rc = ffn_down_possible(d))) return rc;
+  return ffn_down_launch(d, w, st, hipStream_t(stream));
+}
+
 int dec_layer_step(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st,
                    void* stream) {
   int rc;
   const uint32_t f = d ? d->flags : 0u;
   const bool split_qkv = f & (DEC_UNFUSED | DEC_NO_FUSE_QKV);
   const bool split_ffn = f & (DEC_UNFUSED | DEC_NO_FUSE_FFN);
+  const bool fuse_down = (f & DEC_FUSE_DOWN) && !split_ffn;
   if ((rc = check_desc(d)) || (rc = check_weights(d, w)) || (rc = check_state(st, split_qkv || split_ffn))) return rc;
+  if (fuse_down && (rc = ffn_down_possible(d))) return rc;
   hipStream_t s = hipStream_t(stream);
   const int H = d->hidden, F = d->ffn, qd = d->n_q_heads * d->head_dim;
   if ((rc = split_qkv ? qkv_unfused(d, w, st, s) : qkv_launch(d, w, st, s))) return rc;
@@ -464,6 +531,7 @@ int dec_layer_step(const dec_layer_desc* d, const dec_layer_weights* w, const de
     if ((rc = attn_launch(d, st, s))) return rc;
     if ((rc = residual_launch(d, w->wo, H, qd, st->attn, st->x, s))) return rc;
   }
+  if (fuse_down) return ffn_down_launch(d, w, st, s);
   if ((rc = split_ffn ? ffn_unfused(d, w, st, s) : ffn_launch(d, w->ffn_norm, w->wgate, w->wup, st->x, st->h, s)))
     return rc;
   return residual_launch(d, w->wdown, H, F, st->h, st->x, s);

@@ -64,19 +64,6 @@ __device__ __forceinline__ uint16_t pack_i8_pair(float c0, float c1) {
   return uint16_t(uint8_t(int8_t(int(c0)))) | uint16_t(uint16_t(uint8_t(int8_t(int(c1)))) << 8);
 }
 
-// Two floats as one agent-scope atomic store (8-byte aligned address).
-__device__ __forceinline__ void store_pair_agent(float* p, float lo, float hi) {
-  const uint64_t v = uint64_t(__float_as_uint(lo)) | (uint64_t(__float_as_uint(hi)) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Two floats with one agent-scope atomic load (8-byte aligned address).
-__device__ __forceinline__ float2 load_pair_agent(const float* p) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
-}
-
 // LDS the finish step reads or uses: the per-wave output sums
 // ored [NW][G][D], the split's (m, l) stat [G][2], and the combine's
 // scratch: wts [kSplitMax][G], den [G], accs [NW * 64], role.

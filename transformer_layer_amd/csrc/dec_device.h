@@ -105,6 +105,21 @@ __device__ __forceinline__ float fold_groups(float v) {
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
+// Data other workgroups of the same launch read or wrote (they may run on
+// other XCDs, whose L2 caches are not coherent with this one): two floats
+// as one agent-scope atomic store (8-byte aligned address).
+__device__ __forceinline__ void store_pair_agent(float* p, float lo, float hi) {
+  const uint64_t v = uint64_t(__float_as_uint(lo)) | (uint64_t(__float_as_uint(hi)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Two floats with one agent-scope atomic load (8-byte aligned address).
+__device__ __forceinline__ float2 load_pair_agent(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 __device__ __forceinline__ float swiglu(float g, float u) { return silu(g) * u; }
 

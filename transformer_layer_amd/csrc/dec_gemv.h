@@ -20,6 +20,9 @@
 //   EPI_SWIGLU    h[j] = silu(Wg[j] u) * (Wu[j] u)             (gated FFN)
 //   EPI_STORE2    y[j] = Wg[j] u, y2[j] = Wu[j] u              (per-op gate/up)
 //   EPI_NORM_STORE  y[r] = W norm(x) (final RMSNorm + LM head logits)
+//   EPI_SWIGLU_PUB  as EPI_SWIGLU, h stored with agent-scope stores, so that
+//                 workgroups on other XCDs can read it in the same launch
+//                 (the gated FFN with the down projection folded in)
 #pragma once
 
 #include "dec_device.h"
@@ -32,7 +35,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 struct WF32 { static constexpr int GE = 4; static constexpr int ID = 0; };
 struct WBF16 { static constexpr int GE = 8; static constexpr int ID = 1; };
 
-enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_STORE2 = 4, EPI_NORM_STORE = 5 };
+enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_STORE2 = 4, EPI_NORM_STORE = 5,
+       EPI_SWIGLU_PUB = 6 };
+
+// epilogues whose prologue is the RMSNorm of the input
+__host__ __device__ constexpr bool epi_has_norm(int epi) {
+  return epi == EPI_QKV || epi == EPI_SWIGLU || epi == EPI_SWIGLU_PUB || epi == EPI_NORM_STORE;
+}
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -97,7 +106,7 @@ __device__ __forceinline__ void load_norm_granule(const void* g, int ntype, int 
 // is stored the same way whichever kernel computed it.
 template <int EPI>
 struct PairEpi {
-  static constexpr bool PAIRED = (EPI == EPI_SWIGLU || EPI == EPI_STORE2);  // rows from two matrices
+  static constexpr bool PAIRED = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_PUB || EPI == EPI_STORE2);  // rows from two matrices
   static constexpr bool CONSEC = (EPI == EPI_STORE || EPI == EPI_RESIDUAL || EPI == EPI_NORM_STORE);
 
   static __device__ __forceinline__ int npairs(const GemvArgs& a) {
@@ -152,6 +161,8 @@ struct PairEpi {
       if (v1) a.x[r1] = e1 + y1;
     } else if constexpr (EPI == EPI_SWIGLU) {
       a.y[r0] = swiglu(y0, y1);
+    } else if constexpr (EPI == EPI_SWIGLU_PUB) {
+      __hip_atomic_store(a.y + r0, swiglu(y0, y1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else if constexpr (EPI == EPI_STORE2) {
       a.y[r0] = y0;
       a.y2[r0] = y1;
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(gemv_min
 void gemv_kernel(GemvArgs a) {
   constexpr int GE = T::GE;
   constexpr int NR = 2 * NP;  // rows per task
-  constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_NORM_STORE);
+  constexpr bool NORM = epi_has_norm(EPI);
   using PE = PairEpi<EPI>;
   constexpr bool PAIRED = PE::PAIRED;
   constexpr int TPW = kWaves / KS;  // tasks per workgroup iteration

@@ -95,6 +95,16 @@ inline bool q4mfma_plan(int cols, int ntiles, int* nw, int* spw) {
 
 enum GemvEpi { kEpiStore = 0, kEpiResidual = 1, kEpiQkv = 2, kEpiSwiglu = 3, kEpiStore2 = 4, kEpiNormStore = 5 };
 
+// The gated FFN with the down projection folded in (4-bit weights,
+// dec_ffn_down.hip): f as for the gated FFN, dn as for the down projection
+// (input f.y = h); bar = two zeroed counter words. Check: hipSuccess if the
+// kernel can run the shape with every workgroup resident on this device,
+// hipErrorInvalidValue for a shape outside its plans,
+// hipErrorInvalidConfiguration when the workgroups would not all fit.
+constexpr int kFfnDownBarWord = 2;   // words 2 and 3 of the first counter line
+hipError_t ffn_down_q4_check(const GemvArgs& f, const GemvArgs& dn);
+hipError_t launch_ffn_down_q4(const GemvArgs& f, const GemvArgs& dn, uint32_t* bar, int no_wait, hipStream_t s);
+
 // Launch the GEMV core for weight type wtype (0 f32, 1 bf16, 2 q4).
 hipError_t launch_gemv_f32(int epi, const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemv_bf16(int epi, const GemvArgs& a, hipStream_t s);

@@ -197,37 +197,67 @@ __device__ __forceinline__ void q4mfma_quantize(const GemvArgs& a, float r, cons
 __device__ __forceinline__ int q4_hi16(uint32_t w) { return int(w & 0xf0f0f0f0u); }
 __device__ __forceinline__ int q4_lo16(uint32_t w) { return int((w << 4) & 0xf0f0f0f0u); }
 
+// One workgroup's share of a 4-bit GEMV: TT tiles of 16 rows, the input as
+// digits in LDS, NW waves splitting each tile's steps. The kernels below
+// compose its steps: request the input, the tiles' scales and weights; the
+// prologue (RMSNorm for the fused epilogues, the digits, the staged scales);
+// then each tile's products and epilogue.
 template <int EPI, int NW, int SPW, int TT>
-__global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
+struct Q4Tiles {
   using PE = PairEpi<EPI>;
-  constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_NORM_STORE);
+  static constexpr bool NORM = epi_has_norm(EPI);
   static_assert(NW >= 4, "the sum of squares uses the first four waves");
-  extern __shared__ __align__(16) uint8_t smem[];
+  // block scales of a wave's steps (4 SPW blocks from block 4 s0) for a
+  // tile's 16 rows. In LDS mode: row-contiguous 2-byte loads (KL lanes per
+  // row, so a load touches few cache lines) written to LDS, where each step
+  // reads its lane's scale. Otherwise each lane loads the scale of each of
+  // its steps (a 32-bit register per scale: two 16-bit values packed in one
+  // register would make each load wait for the previous one).
+  static constexpr bool SL = q4mfma_scales_in_lds(SPW);
+  static constexpr int KB = 4 * SPW;                               // blocks per row of a wave's share
+  static constexpr int KL = KB <= 16 ? 16 : KB <= 32 ? 32 : 64;    // lanes per row in a load
+  static constexpr int NSL = SL ? 16 * KL / 64 : SPW;              // scale loads per tile
+  static constexpr int GQ = q4mfma_groups<NW, SPW>();             // input groups per quantizing thread
 
-  if (a.null_kernel) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15;   // MFMA column: row n of the tile
-  const int g = lane >> 4;   // k-group: block 4s + g of a step
+  const GemvArgs& a;
+  int tid, lane, wv, n, g;   // n: MFMA column (row n of the tile); g: k-group (block 4s + g of a step)
+  int G, S, GP;              // blocks per row, steps of four blocks, blocks with padding
+  uint8_t* dig;              // [GP][3][2][16] digits
+  int* ex;                   // [GP] exponents E_b
+  float* red;                // [2][NW][16] cross-wave sums
+  float* ssq;                // [4] sums of squares
+  uint8_t* zero16;           // 16 zero bytes
+  uint16_t* scl;             // this wave's staged scales [TT][16][KB]
+  size_t row_bytes;
+  int npairs, s0, ns;        // row pairs; this wave's first step and step count (wave-uniform)
 
-  const int G = a.cols / 32;       // blocks per row
-  const int S = (G + 3) / 4;       // steps of four blocks
-  const int GP = 4 * S;            // blocks with padding
-  uint8_t* dig = smem;                                                      // [GP][3][2][16]
-  int* ex = reinterpret_cast<int*>(smem + size_t(GP) * 96);                 // [GP] exponents E_b
-  float* red = reinterpret_cast<float*>(ex + GP);                           // [2][NW][16]
-  float* ssq = red + 2 * NW * 16;                                           // [4]
-  uint8_t* zero16 = reinterpret_cast<uint8_t*>(ssq + 4);                    // 16 zero bytes
+  __device__ __forceinline__ Q4Tiles(const GemvArgs& args, uint8_t* smem) : a(args) {
+    tid = threadIdx.x;
+    lane = tid & 63;
+    wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    n = lane & 15;
+    g = lane >> 4;
+    G = a.cols / 32;
+    S = (G + 3) / 4;
+    GP = 4 * S;
+    dig = smem;
+    ex = reinterpret_cast<int*>(smem + size_t(GP) * 96);
+    red = reinterpret_cast<float*>(ex + GP);
+    ssq = red + 2 * NW * 16;
+    zero16 = reinterpret_cast<uint8_t*>(ssq + 4);
+    scl = reinterpret_cast<uint16_t*>(zero16 + 16) + wv * TT * 16 * KB;
+    row_bytes = size_t(a.cols) / 2;
+    npairs = PE::npairs(a);
+    s0 = wv * SPW;
+    ns = max(0, min(S - s0, SPW));
+  }
 
-  const size_t row_bytes = size_t(a.cols) / 2;
-  const int npairs = PE::npairs(a);
-  const int s0 = wv * SPW;
-  const int ns = max(0, min(S - s0, SPW));   // steps of this wave (wave-uniform)
+  // the first four waves quantize the input
+  __device__ __forceinline__ bool quant() const { return tid < 256; }
 
   // row c (0..15) of a tile: the first or second row of pair c % 8, in the
   // first matrix or (gate/up pairs, c >= 8) the second
-  auto row_at = [&](int tile, int c, bool& second) {
+  __device__ __forceinline__ int row_at(int tile, int c, bool& second) const {
     int p = tile * 8 + (c & 7);
     p = p < npairs ? p : npairs - 1;   // a tile past the last: valid rows, never stored
     int r0, r1;
@@ -235,36 +265,25 @@ __global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
     int r = c < 8 ? r0 : r1;
     second = PE::PAIRED && c >= 8;
     return r < a.rows ? r : a.rows - 1;
-  };
-  // weights of this lane's row in each of the workgroup's TT tiles, for this
-  // wave's steps
-  u32x4 wq[TT][SPW];
-  auto load_tile = [&](int tile, u32x4 (&w)[SPW]) {
+  }
+
+  // weights of this lane's row of a tile, for this wave's steps. Every load
+  // is issued (steps past this wave's share read a valid block and are not
+  // used), so the compiler's count of loads in flight is exact and a wait
+  // for one tile never waits for a later one.
+  __device__ __forceinline__ void load_tile(int tile, u32x4 (&w)[SPW]) const {
     bool second;
     const int r = row_at(tile, n, second);
     const uint8_t* W = reinterpret_cast<const uint8_t*>(second ? a.W2 : a.W) + size_t(r) * row_bytes;
-    // every load is issued (steps past this wave's share read a valid block
-    // and are not used), so the compiler's count of loads in flight is exact
-    // and a wait for one tile never waits for a later one
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       int b = 4 * (s0 + i) + g;
       b = b < G ? b : G - 1;   // padding blocks: any row bytes (their digits are zero)
       w[i] = ldg16(W + size_t(b) * 16);
     }
-  };
-  // block scales of this wave's steps (4 SPW blocks from block 4 s0) for the
-  // tile's 16 rows. In LDS mode: row-contiguous 2-byte loads (KL lanes per
-  // row, so a load touches few cache lines) written to LDS, where each step
-  // reads its lane's scale. Otherwise each lane loads the scale of each of
-  // its steps (a 32-bit register per scale: two 16-bit values packed in one
-  // register would make each load wait for the previous one).
-  constexpr bool SL = q4mfma_scales_in_lds(SPW);
-  constexpr int KB = 4 * SPW;                       // blocks per row of a wave's share
-  constexpr int KL = KB <= 16 ? 16 : KB <= 32 ? 32 : 64;   // lanes per row in a load
-  constexpr int NSL = SL ? 16 * KL / 64 : SPW;      // scale loads per tile
-  uint32_t sv[TT][NSL];
-  auto load_scales = [&](int tile, uint32_t (&v)[NSL]) {
+  }
+
+  __device__ __forceinline__ void load_scales(int tile, uint32_t (&v)[NSL]) const {
     if constexpr (SL) {
 #pragma unroll
       for (int k = 0; k < NSL; ++k) {
@@ -285,80 +304,83 @@ __global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
         v[i] = reinterpret_cast<const uint16_t*>(second ? a.S2 : a.S)[size_t(r) * G + b];
       }
     }
-  };
-  uint16_t* scl = reinterpret_cast<uint16_t*>(zero16 + 16) + wv * TT * 16 * KB;   // [TT][16][KB]
-
-  // the input first (it returns before the weights), then the scales of the
-  // workgroup's tiles and the weights of its first tile
-  constexpr int GQ = q4mfma_groups<NW, SPW>();
-  float4 xv[GQ];
-  uint4 gv[GQ];
-  const bool quant = tid < 256;   // the first four waves quantize the input
-  if (quant) {
-    if (!NORM)
-      q4mfma_load_input<false, 0, GQ>(a, tid, xv, gv);
-    else if (a.ntype == 1)
-      q4mfma_load_input<true, 1, GQ>(a, tid, xv, gv);
-    else
-      q4mfma_load_input<true, 0, GQ>(a, tid, xv, gv);
   }
-  const int tile0 = blockIdx.x * TT;
+
+  // the input groups of a quantizing thread (and, with NORM, the norm
+  // weights); AGENT: with agent-scope loads, for an input other workgroups
+  // of the same launch wrote
+  template <bool AGENT = false>
+  __device__ __forceinline__ void load_input(float4 (&xv)[GQ], uint4 (&gv)[GQ]) const {
+    if constexpr (AGENT) {
+      static_assert(!NORM, "agent-scope input without a norm");
+      const int nf = a.cols / 4;
 #pragma unroll
-  for (int t = 0; t < TT; ++t) load_scales(tile0 + t, sv[t]);
-  load_tile(tile0, wq[0]);   // the second tile's weights: once the input is quantized
-
-  // the position (QKV epilogue) is checked once the first tile's weights are
-  // requested: read first, its round trip delayed every request of the
-  // workgroup (9B-shaped 4-bit stack +0.9% tokens/s)
-  int pos = 0;
-  if constexpr (EPI == EPI_QKV) {
-    if (!qkv_pos_ok(a, pos)) return;
+      for (int i = 0; i < GQ; ++i) {
+        const int f = tid + 256 * i;
+        const int fc = f < nf ? f : nf - 1;
+        const float2 lo = load_pair_agent(a.in + 4 * fc);
+        const float2 hi = load_pair_agent(a.in + 4 * fc + 2);
+        xv[i] = make_float4(lo.x, lo.y, hi.x, hi.y);
+      }
+    } else if constexpr (!NORM) {
+      q4mfma_load_input<false, 0, GQ>(a, tid, xv, gv);
+    } else if (a.ntype == 1) {
+      q4mfma_load_input<true, 1, GQ>(a, tid, xv, gv);
+    } else {
+      q4mfma_load_input<true, 0, GQ>(a, tid, xv, gv);
+    }
   }
 
-  // ---- prologue: RMSNorm (fused kernels), then the input as digits in LDS
-  if (tid == 0) *reinterpret_cast<i32x4*>(zero16) = i32x4{0, 0, 0, 0};
-  float r = 1.0f;
-  if constexpr (NORM) {
-    if (quant) {
-      const float ss = q4mfma_sumsq_regs<GQ>(xv, a.cols / 4, tid);
-      if (lane == 0) ssq[wv] = ss;
+  // RMSNorm (fused epilogues), then the input as digits in LDS and the
+  // tiles' scales staged; ends with a workgroup barrier
+  __device__ __forceinline__ void prologue(const float4 (&xv)[GQ], const uint4 (&gv)[GQ],
+                                           const uint32_t (&sv)[TT][NSL]) const {
+    if (tid == 0) *reinterpret_cast<i32x4*>(zero16) = i32x4{0, 0, 0, 0};
+    float r = 1.0f;
+    if constexpr (NORM) {
+      if (quant()) {
+        const float ss = q4mfma_sumsq_regs<GQ>(xv, a.cols / 4, tid);
+        if (lane == 0) ssq[wv] = ss;
+      }
+      __syncthreads();
+      float ss = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ss += ssq[k];
+      r = 1.0f / sqrtf(ss / float(a.cols) + a.eps);
+    }
+    if (quant()) {
+      if constexpr (!NORM)
+        q4mfma_quantize<false, 0, GQ>(a, r, xv, gv, dig, ex, GP, tid);
+      else if (a.ntype == 1)
+        q4mfma_quantize<true, 1, GQ>(a, r, xv, gv, dig, ex, GP, tid);
+      else
+        q4mfma_quantize<true, 0, GQ>(a, r, xv, gv, dig, ex, GP, tid);
+    }
+    if constexpr (SL) {
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int k = 0; k < NSL; ++k) {
+          const int rr = k * (64 / KL) + lane / KL;
+          const int j = lane % KL;
+          if (j < KB) scl[(t * 16 + rr) * KB + j] = uint16_t(sv[t][k]);
+        }
     }
     __syncthreads();
-    float ss = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) ss += ssq[k];
-    r = 1.0f / sqrtf(ss / float(a.cols) + a.eps);
   }
-  if (quant) {
-    if (!NORM)
-      q4mfma_quantize<false, 0, GQ>(a, r, xv, gv, dig, ex, GP, tid);
-    else if (a.ntype == 1)
-      q4mfma_quantize<true, 1, GQ>(a, r, xv, gv, dig, ex, GP, tid);
-    else
-      q4mfma_quantize<true, 0, GQ>(a, r, xv, gv, dig, ex, GP, tid);
-  }
-  if constexpr (SL) {
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-#pragma unroll
-      for (int k = 0; k < NSL; ++k) {
-        const int rr = k * (64 / KL) + lane / KL;
-        const int j = lane % KL;
-        if (j < KB) scl[(t * 16 + rr) * KB + j] = uint16_t(sv[t][k]);
-      }
-  }
-  __syncthreads();
 
-  // the digit operand of this lane: block 4 s + g, digit p = n % 4 when
-  // n / 4 == g and p < 3 (step i at a stride of four blocks); 16 zero bytes
-  // otherwise
-  const bool has_a = (n >> 2) == g && (n & 3) < 3;
-  const uint8_t* abase = has_a ? dig + ((4 * s0 + g) * 3 + (n & 3)) * 32 : zero16;
-  const int astride = has_a ? 4 * 3 * 32 : 0;
-  const int ahalf = has_a ? 16 : 0;
-  const int* exl = ex + 4 * s0 + g;
-
-  auto run_tile = [&](int tile, int iter, const u32x4 (&w)[SPW], const uint32_t (&sr)[NSL]) {
+  // tile `tile` (the workgroup's iter-th): products, sums over k-groups and
+  // waves, epilogue (ends with the workgroup barrier of the wave sums)
+  __device__ __forceinline__ void run_tile(int tile, int iter, const u32x4 (&w)[SPW], const uint32_t (&sr)[NSL],
+                                           int pos) const {
+    // the digit operand of this lane: block 4 s + g, digit p = n % 4 when
+    // n / 4 == g and p < 3 (step i at a stride of four blocks); 16 zero
+    // bytes otherwise
+    const bool has_a = (n >> 2) == g && (n & 3) < 3;
+    const uint8_t* abase = has_a ? dig + ((4 * s0 + g) * 3 + (n & 3)) * 32 : zero16;
+    const int astride = has_a ? 4 * 3 * 32 : 0;
+    const int ahalf = has_a ? 16 : 0;
+    const int* exl = ex + 4 * s0 + g;
     const uint16_t* sl = scl + (iter * 16 + n) * KB + g;   // LDS mode, step i: block 4 i + g of row n
     float e0 = 0.0f, e1 = 0.0f;
     if (wv == 0 && lane < 8) PE::inputs(a, pos, tile * 8 + lane, e0, e1);
@@ -394,15 +416,45 @@ __global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
       const float y1 = dpp_mov<0x128>(y);   // row n + 8 of the tile: the pair's second row
       if (lane < 8) PE::finish(a, pos, tile * 8 + lane, y, y1, e0, e1);
     }
-  };
+  }
+};
 
-  // several tiles per workgroup: tiles blockIdx.x, + gridDim.x, ..., two
-  // tiles' weights in flight; a buffer is refilled with the tile after next
-  // as soon as its tile is done
+template <int EPI, int NW, int SPW, int TT>
+__global__ __launch_bounds__(NW * 64) void q4mfma_kernel(GemvArgs a) {
+  using T = Q4Tiles<EPI, NW, SPW, TT>;
+  extern __shared__ __align__(16) uint8_t smem[];
+
+  if (a.null_kernel) return;
+  const T q(a, smem);
+
+  // the input first (it returns before the weights), then the scales of the
+  // workgroup's tiles and the weights of its first tile
+  float4 xv[T::GQ];
+  uint4 gv[T::GQ];
+  if (q.quant()) q.load_input(xv, gv);
+  const int tile0 = blockIdx.x * TT;
+  uint32_t sv[TT][T::NSL];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) q.load_scales(tile0 + t, sv[t]);
+  u32x4 wq[TT][SPW];
+  q.load_tile(tile0, wq[0]);   // the second tile's weights: once the input is quantized
+
+  // the position (QKV epilogue) is checked once the first tile's weights are
+  // requested: read first, its round trip delayed every request of the
+  // workgroup (9B-shaped 4-bit stack +0.9% tokens/s)
+  int pos = 0;
+  if constexpr (EPI == EPI_QKV) {
+    if (!qkv_pos_ok(a, pos)) return;
+  }
+
+  q.prologue(xv, gv, sv);
+
+  // several tiles per workgroup: two tiles' weights in flight; a buffer is
+  // refilled with the tile after next as soon as its tile is done
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    if (t + 1 < TT) load_tile(tile0 + t + 1, wq[t + 1]);
-    run_tile(tile0 + t, t, wq[t], sv[t]);
+    if (t + 1 < TT) q.load_tile(tile0 + t + 1, wq[t + 1]);
+    q.run_tile(tile0 + t, t, wq[t], sv[t], pos);
   }
 }
 

@@ -20,6 +20,7 @@ DEC_NO_FUSE_QKV = 0x4
 DEC_NO_FUSE_FFN = 0x8
 DEC_NO_FUSE_ATTN_O = 0x10
 DEC_DETERMINISTIC = 0x20
+DEC_FUSE_DOWN = 0x40
 DEC_ATTN_KERNEL_MASK = 0x3000
 DEC_ATTN_BATCHED = 0x1000
 DEC_ATTN_STREAM = 0x2000
@@ -31,7 +32,7 @@ DEC_TEST_DROP_SPLIT = 0x800
 DEC_ERR_POS = 0x1
 DEC_ERR_TOKEN = 0x2
 DEC_ERR_SYNC = 0x4
-ABI_VERSION = 5
+ABI_VERSION = 6
 DEC_COUNTER_STRIDE = 16
 DEC_STATIC_SCRATCH_BYTES = 4 << 20
 
@@ -79,6 +80,7 @@ SIGNATURES = {
     "dec_attn_o_residual": (ctypes.c_int, [P_DESC, dec_mat, P_ST, c_void_p]),
     "dec_gemv_residual": (ctypes.c_int, [P_DESC, dec_mat, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "dec_gated_ffn": (ctypes.c_int, [P_DESC, c_void_p, dec_mat, dec_mat, c_void_p, c_void_p, c_void_p]),
+    "dec_gated_ffn_down": (ctypes.c_int, [P_DESC, P_W, P_ST, c_void_p]),
     "dec_layer_step": (ctypes.c_int, [P_DESC, P_W, P_ST, c_void_p]),
     "dec_layer_step_static": (ctypes.c_int, [P_DESC, P_W, P_ST, c_void_p]),
     "dec_lm_head": (ctypes.c_int, [P_DESC, c_int32, c_void_p, dec_mat, c_int32, c_void_p, c_void_p, c_void_p,
@@ -194,6 +196,11 @@ def dec_gemv_residual(desc, w: dec_mat, rows: int, cols: int, inp: int, x: int, 
 
 def dec_gated_ffn(desc, ffn_norm: int, wgate: dec_mat, wup: dec_mat, x: int, h: int, stream=None) -> None:
     _check(load().dec_gated_ffn(ctypes.byref(desc), ffn_norm, wgate, wup, x, h, _s(stream)), "dec_gated_ffn")
+
+
+def dec_gated_ffn_down(desc, weights, state, stream=None) -> None:
+    _check(load().dec_gated_ffn_down(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(state),
+                                     _s(stream)), "dec_gated_ffn_down")
 
 
 def dec_layer_step(desc, weights, state, stream=None) -> None:
