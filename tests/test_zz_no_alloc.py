@@ -59,6 +59,7 @@ CASES = [
     ("C4", L.DEC_DETERMINISTIC, 4099, True),
     ("C2", 0, 515, False),
     ("C1", L.DEC_UNFUSED, 19, True),          # the per-op intermediates in the static array
+    ("C5", L.DEC_FUSE_DOWN, 8195, True),      # the FFN + down kernel's grid counter words in the static array
 ]
 
 
