@@ -68,7 +68,7 @@ enum dec_status {
   DEC_E_DTYPE = -3,       /* unsupported element type for this argument */
   DEC_E_ALIGN = -4,       /* a pointer is not 16-byte aligned */
   DEC_E_LAUNCH = -5,      /* the HIP runtime rejected a launch */
-  DEC_E_UNSUPPORTED = -6  /* valid request this build does not implement */
+  DEC_E_UNSUPPORTED = -6  /* valid request the library does not implement */
 };
 
 /* uint32 words per kv head in dec_layer_state.counters: kv head j uses words
