@@ -119,6 +119,7 @@ def _pins_that_should_fail():
         pins.test_i8_cache_row_fixture,
         pins.test_i8_cache_rows_round_to_nearest_step,
         lambda: pins.test_decode_equals_dense_causal_forward("bf16", 8, 2, "i8"),
+        lambda: pins.test_greedy_sequence_equals_dense_forward_greedy("bf16", "bf16"),
     ]
 
 
@@ -265,3 +266,22 @@ def test_planted_off_by_one_and_missing_residual_fail_a_pin(monkeypatch):
                 except AssertionError:
                     failed += 1
             assert failed, f"no pin caught the planted {attr} mistake"
+
+
+def test_planted_head_mistakes_fail_the_greedy_pin(monkeypatch):
+    """Mistakes in the per-token tail: logits from x without the final
+    RMSNorm, and the argmax taken over the logits shifted by one index."""
+    def logits_no_norm(self, x):
+        return ref.gemv(self.gw("head"), x)
+
+    def greedy_shifted(self, x):
+        z = self.logits(x)
+        i = int(np.argmax(z[1:]))
+        top2 = np.partition(z, -2)[-2:]
+        return i, float(top2[1] - top2[0])
+
+    for attr, repl in (("logits", logits_no_norm), ("greedy", greedy_shifted)):
+        with monkeypatch.context() as m:
+            m.setattr(ref.Oracle, attr, repl)
+            with pytest.raises(AssertionError):
+                pins.test_greedy_sequence_equals_dense_forward_greedy("bf16", "bf16")

@@ -328,6 +328,37 @@ def test_decode_equals_dense_causal_forward(kind, nq, nkv, kv):
     assert _rel(out, ref) < 1e-12
 
 
+@pytest.mark.parametrize("kind,kv", [("bf16", "bf16"), ("q4", "i8")])
+def test_greedy_sequence_equals_dense_forward_greedy(kind, kv):
+    """The greedy token sequence as a whole: the oracle decoding token by
+    token (embedding, layers, final norm, head, argmax fed back) against a
+    loop that re-runs the dense causal forward over the whole prefix each
+    step and takes torch's final rms_norm, the head product and
+    torch.argmax (first index of the maximum). Tokens equal, logits within
+    1e-12."""
+    cfg = synth.tiny(n_layers=2, hidden=64, n_q_heads=8, n_kv_heads=2, head_dim=16, ffn=96, wtype=kind,
+                     ntype="bf16", kvtype=kv, htype="bf16", rope_theta=10000.0, ctx=0, steps=10, seed=23)
+    o = oracle.Oracle.from_config(cfg)
+    T = cfg.steps
+    tok = int(synth.tokens(cfg)[0])
+    got, got_logits = [tok], []
+    for p in range(T - 1):
+        x = o.step(got[-1], p)[-1]
+        got_logits.append(o.logits(x))
+        got.append(o.greedy(x)[0])
+    E = torch.from_numpy(np.asarray(o.glob["embed"].data, dtype=np.float64))
+    head = torch.from_numpy(oracle.dequant(o.glob["head"]))
+    gfin = torch.from_numpy(oracle.dequant(o.glob["final_norm"]))
+    ref = [tok]
+    for p in range(T - 1):
+        X = E[torch.tensor(ref)].numpy()
+        h = torch.from_numpy(_dense_causal_forward(cfg, o.layers, X)[-1])
+        z = head @ torch.nn.functional.rms_norm(h, (cfg.hidden,), weight=gfin, eps=cfg.rms_eps)
+        assert _rel(got_logits[p], z.numpy()) < 1e-12, f"step {p}"
+        ref.append(int(torch.argmax(z)))
+    assert got == ref
+
+
 def _run_layers(o, x, p):
     for l in range(len(o.layers)):
         x = o.layer(l, x, p)
