@@ -359,6 +359,18 @@ def test_greedy_sequence_equals_dense_forward_greedy(kind, kv):
     assert got == ref
 
 
+def test_decode_equals_dense_causal_forward_at_depth():
+    """The same over 40 layers (the 9B-shaped stacks' depth) at small widths,
+    4-bit weights and a bf16 cache: depth is repetition, and the agreement
+    holds through it."""
+    cfg = synth.tiny(n_layers=40, hidden=64, n_q_heads=8, n_kv_heads=2, head_dim=16, ffn=96, wtype="q4",
+                     ntype="bf16", kvtype="bf16", rope_theta=10000.0, ctx=0, steps=6, seed=25)
+    o = oracle.Oracle.from_config(cfg, with_globals=False)
+    X = synth.rand_f32((25, 7, 7), (cfg.steps, cfg.hidden)).astype(np.float64)
+    out = np.stack([_run_layers(o, X[t], t) for t in range(cfg.steps)])
+    assert _rel(out, _dense_causal_forward(cfg, o.layers, X)) < 1e-11
+
+
 def _run_layers(o, x, p):
     for l in range(len(o.layers)):
         x = o.layer(l, x, p)
