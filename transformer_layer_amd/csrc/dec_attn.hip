@@ -405,7 +405,7 @@ static hipError_t go_attn(const AttnArgs& a, hipStream_t s) {
 // (rows per step: 64 / lanes-per-row rows per wave, times the waves)
 template <int D, int KVT, int NW>
 static hipError_t go_attn_vl(const AttnArgs& a, hipStream_t s) {
-  constexpr int rows_per_step = (kWave / (D * (KVT == 1 ? 2 : 4) / 16)) * NW;
+  constexpr int rows_per_step = (kWave / (D * (KVT == 1 ? 2 : KVT == 2 ? 1 : 4) / 16)) * NW;
   return a.chunk > rows_per_step ? go_attn<D, KVT, NW, true>(a, s) : go_attn<D, KVT, NW, false>(a, s);
 }
 
