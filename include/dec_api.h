@@ -113,7 +113,8 @@ enum dec_status {
 #define DEC_ATTN_BATCHED 0x1000u /* rows in registers in batches, one softmax per workgroup
                                     through LDS (any cache type; chunks up to 256) */
 #define DEC_ATTN_STREAM 0x2000u  /* keys scored as they arrive, values staged in LDS
-                                    (chunks whose values fit in LDS) */
+                                    (chunks whose values fit in LDS; int8 caches: at
+                                    most 256, at most four query heads per kv head) */
 #define DEC_ATTN_LOCAL 0x3000u   /* every row requested at launch, a softmax per wave,
                                     waves rescaled once (bf16 cache; chunks up to 9 row
                                     steps of eight waves: 288 positions at d = 128) */

@@ -210,8 +210,7 @@ def test_bad_descriptor_is_rejected(L, field, value, code, word):
     ("DEC_ATTN_LOCAL", {"kvtype": 0}),                        # the wave-local kernel reads bf16 caches only
     ("DEC_ATTN_STREAM", {"kvtype": 0, "n_q_heads": 64, "attn_chunk": 256}),  # f32 values beyond LDS
     ("DEC_ATTN_BATCHED", {"max_ctx": 100000}),                # 391 splits of at most 256 positions
-    ("DEC_ATTN_STREAM", {"kvtype": 3}),                       # an int8 cache is read by the batched kernel only
-    ("DEC_ATTN_LOCAL", {"kvtype": 3}),
+    ("DEC_ATTN_LOCAL", {"kvtype": 3}),                        # nor an int8 one
 ])
 def test_attention_kernel_that_cannot_run_the_shape_is_refused(L, kernel, over):
     d = desc_of(L, synth.CONFIGS["C4"], flags=getattr(L, kernel), **over)

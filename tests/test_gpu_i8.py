@@ -140,6 +140,31 @@ def test_int8_cache_fused_and_per_op_4bit_agree_bit_for_bit(gpu):
     assert torch.equal(Ka, Kb) and torch.equal(Va, Vb)
 
 
+def test_9b_shaped_bf16_stack_with_int8_cache_at_4096_positions(gpu):
+    """Two layers of the 9B-shaped bf16 stack with an int8 cache prefilled
+    over 4096 positions, three tokens (the streaming attention kernel, its
+    partials combined in the output projection), layer by layer."""
+    cfg = synth.CONFIGS["C4"].with_(kvtype="i8", n_layers=2)
+    st = DecodeStack(cfg)
+    layers = [synth.layer_weights(cfg, l) for l in range(cfg.n_layers)]
+    embed = synth.embedding(cfg)
+    o = oracle.Oracle(cfg, layers, glob={"embed": embed})
+    for l, lw in enumerate(layers):
+        st.set_layer(l, lw)
+        K, V = synth.prefill(cfg, l)
+        st.set_prefill(l, K, V)
+        o.load_prefill(l, K, V)
+    st.set_embedding(embed)
+    st.attn.fill_(float("nan"))
+    toks = synth.tokens(cfg)
+    worst, flips = _decode_and_compare(cfg, st, o, [cfg.ctx, cfg.ctx + 1, cfg.ctx + 2], toks)
+    print(f"9B-shaped bf16, int8 cache at {cfg.ctx}: worst layer relative L2 {worst:.2e}, {flips} codes differed")
+    assert st.check_err() == 0
+    assert worst <= TOL
+    # the combine ran in the output projection: the attention output buffer was never written
+    assert bool(torch.isnan(st.attn).all())
+
+
 def test_9b_shaped_4bit_stack_with_int8_cache_at_8192_positions(gpu):
     """Two layers of the 9B-shaped 4-bit stack with an int8 cache prefilled
     over 8192 positions, one token at 8192, layer by layer."""

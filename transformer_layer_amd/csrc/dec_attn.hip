@@ -330,12 +330,13 @@ static int wide_default_chunk(int n_kv, int max_ctx, int cmax) {
 
 bool attn_plan(int n_q, int n_kv, int head_dim, int kvtype, int max_ctx, int chunk_req, int kind_req, int* chunk,
                int* nsplit, int* waves, int* kind) {
-  // an int8 cache runs on the batched kernel only (128-wide heads)
+  // an int8 cache runs on the batched and streaming kernels (128-wide heads;
+  // streamed chunks of at most kChunkMax rows)
   const bool i8 = kvtype == 2;
-  const int smax = i8 ? 0 : attn_lds_max_chunk(n_q, n_kv, head_dim, kvtype);   // streaming kernel: 0 if none fits
+  int smax = attn_lds_max_chunk(n_q, n_kv, head_dim, kvtype);   // streaming kernel: 0 if none fits
+  if (i8 && smax > kChunkMax) smax = kChunkMax;
   const int lmax = kvtype == 1 ? attn_local_max_chunk(head_dim, kvtype) : 0;
   int k = kind_req;
-  if (i8 && k == kAttnDefault) k = kAttnBatched;
   if (k == kAttnDefault) {
     if (chunk_req > 0) {
       // a requested chunk: the streaming kernel when its values fit in LDS

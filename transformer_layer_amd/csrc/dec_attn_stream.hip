@@ -17,16 +17,27 @@
 // wait in LDS for the softmax; only the chunk's values, its scores and the
 // reduction scratch live there.
 //
+// An int8 cache (KVT 2): the rows hold codes, and the key waves also load
+// the chunk's row scales into LDS; the softmax pass applies them (score =
+// code dot product times the key scale; the sum of p * v reads p times the
+// value scale). The token's own row is not read from the cache: the split
+// holding position p streams one row fewer, and wave 0 quantizes the staged
+// float k and v rows (the batched kernel's rule), stores codes and scales
+// into slot p of the cache, and puts the token's code score, its scales and
+// its value codes into the LDS row the cache would have filled, so the
+// softmax and the sum treat it like any other row.
+//
 // LDS layout (bytes), rows padded to cpad (a whole number of eight-wave
 // row steps): [values cpad x row][scores G x cpad f32][per-wave output sums
-// NW x G x D f32][combine scratch][(m, l) G x 2 f32][role].
+// NW x G x D f32][combine scratch][(m, l) G x 2 f32][role][int8: key and
+// value scales 2 x cpad f32].
 #include "dec_attn_common.h"
 
 namespace dec {
 
 template <int D, int KVT>
 struct StreamShape {
-  static constexpr int EB = KVT == 1 ? 2 : 4;   // bytes per cache element
+  static constexpr int EB = KVT == 1 ? 2 : KVT == 2 ? 1 : 4;   // bytes per cache element
   static constexpr int RB = D * EB;             // bytes per cache row
   static constexpr int DPL = 16 / EB;           // dims per lane (16 bytes)
   static constexpr int LPR = D / DPL;           // lanes per row
@@ -40,8 +51,9 @@ constexpr int kRing = 8;   // loads in flight per lane
 __host__ __device__ constexpr int stream_comb_bytes(int G) {
   return ((kSplitMax * G + G) * 4 + 15) / 16 * 16 + kLdsWaves * 64 * 16;
 }
-__host__ __device__ constexpr int stream_lds_bytes(int cpad, int rb, int G, int D) {
-  return cpad * rb + G * cpad * 4 + kLdsWaves * G * D * 4 + stream_comb_bytes(G) + G * 2 * 4 + 16;
+__host__ __device__ constexpr int stream_lds_bytes(int cpad, int rb, int G, int D, bool i8) {
+  return cpad * rb + G * cpad * 4 + kLdsWaves * G * D * 4 + stream_comb_bytes(G) + G * 2 * 4 + 16 +
+         (i8 ? 2 * cpad * 4 : 0);
 }
 
 template <int D, int KVT, int G>
@@ -67,6 +79,11 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
   const int t0 = s * a.chunk;
   const int n = min(t0 + a.chunk, L) - t0;
   const int cpad = (a.chunk + RPS - 1) / RPS * RPS;
+  // int8 cache: the split holding the token streams its rows 0 .. n - 2 and
+  // makes row n - 1 from the staged rows
+  constexpr bool I8 = KVT == 2;
+  const bool newrow = I8 && s == ns - 1;
+  const int nc = newrow ? n - 1 : n;   // rows streamed from the cache
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -84,18 +101,21 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
   float4* accs = reinterpret_cast<float4*>(after);                        // [NW * 64]
   float* stat = reinterpret_cast<float*>(after + NW * 64 * 16);           // [G][2]
   int* role = reinterpret_cast<int*>(stat + G * 2);
+  float* ksl = reinterpret_cast<float*>(role + 4);                        // int8: [cpad] key scales
+  float* vsl = ksl + cpad;                                                // int8: [cpad] value scales
 
   // waves 0-3 stream keys, waves 4-7 values: row r of the chunk is read by
   // wave (r / RPW) % 4 of its half at step r / RPH
   const bool keys = wv < 4;
   const int hw = keys ? wv : wv - 4;
-  const int nsteps = (n + RPH - 1) / RPH;
+  const int nsteps = (nc + RPH - 1) / RPH;
+  const int rlast = nc > 0 ? nc - 1 : 0;   // a valid row (slot t0 <= pos) even when none is streamed
   const uint8_t* src = reinterpret_cast<const uint8_t*>(keys ? a.kc : a.vc) +
                        (size_t(j) * a.max_ctx + t0) * RB + li * 16;
   auto row_of = [&](int step) { return step * RPH + hw * RPW + sub; };
   auto load = [&](int step) {
     int r = row_of(step);
-    r = r < n ? r : n - 1;   // every load is issued: past the chunk, its last row again
+    r = r < nc ? r : rlast;   // every load is issued: past the chunk, its last row again
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + size_t(r) * RB));
   };
   // the ring: slot u holds step k0 + u; a consumed slot is refilled at once
@@ -105,6 +125,35 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
   u32x4 ring[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) ring[u] = load(u);
+
+  // int8: the key waves request the chunk's row scales (rows hw * 64 + lane
+  // + 256 k, clamped to the streamed rows; written to LDS once the scores
+  // are done), wave 0 of the token's split the staged k and v rows
+  constexpr int NSC = I8 ? (kChunkMax + 255) / 256 : 1;
+  float rks[NSC], rvs[NSC];
+  float2 kx = {0.0f, 0.0f}, vx = {0.0f, 0.0f};
+  const size_t scale_off = I8 ? kv_i8_scale_off(a.nkv, a.max_ctx, D) : 0;
+  if constexpr (I8) {
+    if (keys) {
+      const float* ksc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.kc) + scale_off) +
+                         size_t(j) * a.max_ctx + t0;
+      const float* vsc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.vc) + scale_off) +
+                         size_t(j) * a.max_ctx + t0;
+#pragma unroll
+      for (int k = 0; k < NSC; ++k) {
+        const int i = min(hw * kWave + lane + 256 * k, rlast);
+        rks[k] = ksc[i];
+        rvs[k] = vsc[i];
+      }
+      if (newrow && wv == 0) {
+        const size_t so = kv_i8_stage_off(a.nkv, a.max_ctx, D);
+        kx = *reinterpret_cast<const float2*>(
+            reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.kc) + so) + size_t(j) * D + 2 * lane);
+        vx = *reinterpret_cast<const float2*>(
+            reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.vc) + so) + size_t(j) * D + 2 * lane);
+      }
+    }
+  }
 
   if (keys) {
     const float qscale = kLog2e / sqrtf(float(D));
@@ -133,8 +182,46 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
 #pragma unroll
             for (int e = 0; e < DPL; ++e) p = fmaf(qv[hh][e], kf[e], p);
             p = group_sum<LPR>(p);
-            if (t < n && li == 0) sc[hh * cpad + t] = p;
+            if (t < nc && li == 0) sc[hh * cpad + t] = p;
           }
+        }
+      }
+    }
+    if constexpr (I8) {
+#pragma unroll
+      for (int k = 0; k < NSC; ++k) {
+        const int i = hw * kWave + lane + 256 * k;
+        if (i < nc) {
+          ksl[i] = rks[k];
+          vsl[i] = rvs[k];
+        }
+      }
+      // the token's row: quantized in float32, stored into slot pos, and
+      // entered as LDS row n - 1 (code score, scales, value codes)
+      static_assert(!I8 || D == 2 * kWave, "int8 cache rows: two dims a lane");
+      if (newrow && wv == 0) {
+        float kc0, kc1, kscale, vc0, vc1, vscale;
+        quantize_pair_i8(kx, kc0, kc1, kscale);
+        quantize_pair_i8(vx, vc0, vc1, vscale);
+        const size_t slot = size_t(j) * a.max_ctx + pos;
+        uint8_t* kcw = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.kc));
+        uint8_t* vcw = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.vc));
+        const uint16_t vpair = pack_i8_pair(vc0, vc1);
+        *reinterpret_cast<uint16_t*>(kcw + slot * D + 2 * lane) = pack_i8_pair(kc0, kc1);
+        *reinterpret_cast<uint16_t*>(vcw + slot * D + 2 * lane) = vpair;
+        *reinterpret_cast<uint16_t*>(vbuf + (n - 1) * RB + 2 * lane) = vpair;
+        if (lane == 0) {
+          *reinterpret_cast<float*>(kcw + scale_off + slot * 4) = kscale;
+          *reinterpret_cast<float*>(vcw + scale_off + slot * 4) = vscale;
+          ksl[n - 1] = kscale;
+          vsl[n - 1] = vscale;
+        }
+        const float qscale = kLog2e / sqrtf(float(D));
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float2 qx = *reinterpret_cast<const float2*>(a.q + (j * G + hh) * D + 2 * lane);
+          const float d = wave_sum(fmaf(qx.x * qscale, kc0, (qx.y * qscale) * kc1));
+          if (lane == 0) sc[hh * cpad + n - 1] = d;
         }
       }
     }
@@ -147,22 +234,23 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
         ring[u] = load(k0 + U + u);
         if (k0 + u < nsteps) {
           const int t = row_of(k0 + u);   // < cpad: the steps cover at most cpad rows
-          *reinterpret_cast<u32x4*>(vbuf + t * RB + li * 16) = w;
+          if (!I8 || t < nc) *reinterpret_cast<u32x4*>(vbuf + t * RB + li * 16) = w;   // int8: row nc is the token's
         }
       }
     }
   }
   __syncthreads();
 
-  // ---- per head: m = max s, p = exp2(s - m), l = sum p
+  // ---- per head: m = max s, p = exp2(s - m), l = sum p (int8: s = code
+  // score x key scale; the sum of p v below reads p x value scale)
   for (int hh = wv; hh < G; hh += NW) {
     float m = -INFINITY;
-    for (int i = lane; i < n; i += kWave) m = fmaxf(m, sc[hh * cpad + i]);
+    for (int i = lane; i < n; i += kWave) m = fmaxf(m, I8 ? sc[hh * cpad + i] * ksl[i] : sc[hh * cpad + i]);
     m = wave_max(m);
     float l = 0.0f;
     for (int i = lane; i < n; i += kWave) {
-      const float p = exp2f(sc[hh * cpad + i] - m);
-      sc[hh * cpad + i] = p;
+      const float p = exp2f((I8 ? sc[hh * cpad + i] * ksl[i] : sc[hh * cpad + i]) - m);
+      sc[hh * cpad + i] = I8 ? p * vsl[i] : p;
       l += p;
     }
     l = wave_sum(l);
@@ -170,36 +258,54 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
   }
   __syncthreads();
 
-  // ---- o = sum_t p_t v_t, all eight waves over the LDS values
-  float o[G][DPL];
+  // ---- o = sum_t p_t v_t, all eight waves over the LDS values. int8 rows
+  // are read eight codes a lane (as many dims as a bf16 lane holds), so the
+  // fold below has the bf16 kernel's width instead of twice its steps.
+  constexpr int PDPL = I8 ? 8 : DPL;    // dims per lane
+  constexpr int PLPR = D / PDPL;        // lanes per row
+  constexpr int PRPW = kWave / PLPR;    // rows per wave read
+  constexpr int PRPS = PRPW * NW;       // rows per step of all eight waves
+  static_assert(PLPR >= 2 && PLPR <= 32, "row layout");
+  const int psub = lane / PLPR;
+  const int pd0 = (lane % PLPR) * PDPL;
+  float o[G][PDPL];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[hh][e] = 0.0f;
-  const int nsteps8 = (n + RPS - 1) / RPS;
+    for (int e = 0; e < PDPL; ++e) o[hh][e] = 0.0f;
+  const int nsteps8 = (n + PRPS - 1) / PRPS;
   for (int b = 0; b < nsteps8; ++b) {
-    const int t = b * RPS + wv * RPW + sub;
+    const int t = b * PRPS + wv * PRPW + psub;
     if (t < n) {
-      float vf[DPL];
-      unpack_row<KVT>(*reinterpret_cast<const u32x4*>(vbuf + t * RB + li * 16), vf);
+      float vf[PDPL];
+      if constexpr (I8) {
+        const uint2 w = *reinterpret_cast<const uint2*>(vbuf + t * RB + pd0);
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi) {
+          vf[bi] = float(int8_t(uint8_t(w.x >> (8 * bi))));
+          vf[4 + bi] = float(int8_t(uint8_t(w.y >> (8 * bi))));
+        }
+      } else {
+        unpack_row<KVT>(*reinterpret_cast<const u32x4*>(vbuf + t * RB + pd0 * (RB / D)), vf);
+      }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         const float p = sc[hh * cpad + t];
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o[hh][e] = fmaf(p, vf[e], o[hh][e]);
+        for (int e = 0; e < PDPL; ++e) o[hh][e] = fmaf(p, vf[e], o[hh][e]);
       }
     }
   }
-  // rows of one wave read sit LPR lanes apart: fold them
+  // rows of one wave read sit PLPR lanes apart: fold them
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[hh][e] = fold_groups<LPR>(o[hh][e]);
-  if (sub == 0)
+    for (int e = 0; e < PDPL; ++e) o[hh][e] = fold_groups<PLPR>(o[hh][e]);
+  if (psub == 0)
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) ored[(wv * G + hh) * D + d0 + e] = o[hh][e];
+      for (int e = 0; e < PDPL; ++e) ored[(wv * G + hh) * D + pd0 + e] = o[hh][e];
   __syncthreads();
 
   attn_finish<D, G, NW>(a, j, s, ns, AttnShared{ored, stat, wts, den, accs, role});
@@ -207,7 +313,7 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
 
 // rows per eight-wave step and bytes per row of a shape
 static void stream_row_shape(int head_dim, int kvtype, int* rps, int* rb) {
-  const int eb = kvtype == 1 ? 2 : 4;
+  const int eb = kvtype == 1 ? 2 : kvtype == 2 ? 1 : 4;
   *rb = head_dim * eb;
   const int lpr = head_dim * eb / 16;
   *rps = (kWave / lpr) * kLdsWaves;
@@ -217,10 +323,12 @@ static bool stream_fits(int n_q, int n_kv, int head_dim, int kvtype, int chunk) 
   int rps, rb;
   stream_row_shape(head_dim, kvtype, &rps, &rb);
   const int cpad = (chunk + rps - 1) / rps * rps;
-  return stream_lds_bytes(cpad, rb, n_q / n_kv, head_dim) <= kLdsBudget;
+  return stream_lds_bytes(cpad, rb, n_q / n_kv, head_dim, kvtype == 2) <= kLdsBudget;
 }
 
 int attn_lds_max_chunk(int n_q, int n_kv, int head_dim, int kvtype) {
+  // int8 rows: 128-wide heads (two dims a lane over a wave), groups of at most four heads
+  if (kvtype == 2 && (head_dim != 128 || n_q / n_kv > 4)) return 0;
   int rps, rb;
   stream_row_shape(head_dim, kvtype, &rps, &rb);
   if (!stream_fits(n_q, n_kv, head_dim, kvtype, rps)) return 0;
@@ -234,14 +342,18 @@ static hipError_t go_attn_stream(const AttnArgs& a, hipStream_t s) {
   using S = StreamShape<D, KVT>;
   const int g = a.nq / a.nkv;
   const int cpad = (a.chunk + S::RPS - 1) / S::RPS * S::RPS;
-  const int lds = stream_lds_bytes(cpad, S::RB, g, D);
+  const int lds = stream_lds_bytes(cpad, S::RB, g, D, KVT == 2);
   if (lds > kLdsBudget) return hipErrorInvalidValue;
   const dim3 grid(a.nkv * a.nsplit), block(kLdsWaves * 64);
   switch (g) {
     case 1: hipLaunchKernelGGL((attn_stream_kernel<D, KVT, 1>), grid, block, lds, s, a); break;
     case 2: hipLaunchKernelGGL((attn_stream_kernel<D, KVT, 2>), grid, block, lds, s, a); break;
     case 4: hipLaunchKernelGGL((attn_stream_kernel<D, KVT, 4>), grid, block, lds, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_stream_kernel<D, KVT, 8>), grid, block, lds, s, a); break;
+    case 8:
+      // int8 rows hold 16 dims a lane: eight heads' queries would not fit in registers
+      if constexpr (KVT == 2) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL((attn_stream_kernel<D, KVT, 8>), grid, block, lds, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -249,8 +361,14 @@ static hipError_t go_attn_stream(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_lds(const AttnArgs& a, hipStream_t s) {
   if (a.nsplit > kSplitMax) return hipErrorInvalidValue;
+  // int8: 128-wide heads, at most kChunkMax rows (the key waves load the scales of 256 rows)
+  if (a.kvtype == 2 && (a.d != 128 || a.chunk > kChunkMax)) return hipErrorInvalidValue;
   if (a.d == 64) return a.kvtype == 1 ? go_attn_stream<64, 1>(a, s) : go_attn_stream<64, 0>(a, s);
-  if (a.d == 128) return a.kvtype == 1 ? go_attn_stream<128, 1>(a, s) : go_attn_stream<128, 0>(a, s);
+  if (a.d == 128) {
+    if (a.kvtype == 2) return go_attn_stream<128, 2>(a, s);
+    return a.kvtype == 1 ? go_attn_stream<128, 1>(a, s) : go_attn_stream<128, 0>(a, s);
+  }
+  if (a.kvtype == 2) return hipErrorInvalidValue;
   return hipErrorInvalidValue;
 }
 
