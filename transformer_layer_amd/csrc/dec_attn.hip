@@ -100,15 +100,35 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     }
   }
 
+  // int8 value rows are read eight codes a lane (the bf16 layout: 16 lanes
+  // a row), so that the fold of the p.v sums below has the bf16 width; 16
+  // codes a lane took three fold steps over twice the accumulators
+  constexpr int VLPR = I8 ? D / 8 : LPR;      // lanes per value row
+  constexpr int VRPS = (kWave / VLPR) * kWaves;  // value rows per workgroup step
+  const int vsub = lane / VLPR;
+  const int vd0 = (lane % VLPR) * 8;          // int8: first code of the lane
+  const int nvsteps = I8 ? (tl - t0 + VRPS - 1) / VRPS : nsteps;
+  auto vrow8 = [&](int step) { return t0 + step * VRPS + wv * (kWave / VLPR) + vsub; };
+  uint2 v8[I8 ? U : 1];
+  auto load_v8 = [&](int step, int u) {
+    const int t = vrow8(step);
+    const bool ok = step < nvsteps && t < tl;
+    v8[u] = ok ? *reinterpret_cast<const uint2*>(vb + size_t(t) * D + vd0) : make_uint2(0u, 0u);
+  };
+
   // first batch of K rows, of V rows (VLATE: once the scores are done),
   // then the queries
-  u32x4 kv[U], vv[U];
+  u32x4 kv[U], vv[I8 ? 1 : U];
   auto first_v = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = row(u);
-      const bool ok = u < nsteps && t < tl;
-      vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
+      if constexpr (I8) {
+        load_v8(u, u);
+      } else {
+        const int t = row(u);
+        const bool ok = u < nsteps && t < tl;
+        vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
+      }
     }
   };
 #pragma unroll
@@ -240,6 +260,46 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   __syncthreads();
 
   // ---- o = sum_t p_t v_t
+  if constexpr (I8) {
+    float o8[G][8];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o8[hh][e] = 0.0f;
+    for (int b = 0; b < nvsteps; b += U) {
+      if (b > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_v8(b + u, u);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = vrow8(b + u);
+        if (b + u < nvsteps && t < tl) {
+          float vf[8];
+#pragma unroll
+          for (int bi = 0; bi < 4; ++bi) {
+            vf[bi] = float(int8_t(uint8_t(v8[u].x >> (8 * bi))));
+            vf[4 + bi] = float(int8_t(uint8_t(v8[u].y >> (8 * bi))));
+          }
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            const float p = sc[hh][t - t0];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o8[hh][e] = fmaf(p, vf[e], o8[hh][e]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o8[hh][e] = fold_groups<VLPR>(o8[hh][e]);
+    if (vsub == 0)
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ored[wv][hh][vd0 + e] = o8[hh][e];
+  } else {
   float o[G][DPL];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
@@ -279,6 +339,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
       for (int e = 0; e < DPL; ++e) ored[wv][hh][d0 + e] = o[hh][e];
+  }
   if constexpr (I8) {
     // the token's own value row (its score is now its weight in sc)
     if (newrow && wv == 0)
