@@ -100,29 +100,34 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // int8 value rows are read eight codes a lane (the bf16 layout: 16 lanes
-  // a row), so that the fold of the p.v sums below has the bf16 width; 16
-  // codes a lane took three fold steps over twice the accumulators
-  constexpr int VLPR = I8 ? D / 8 : LPR;      // lanes per value row
+  // int8 and bf16 value rows are read eight bytes a lane (8 codes or 4
+  // bf16 dims), so the rows of a wave load sit more lanes apart and the fold
+  // of the p.v sums below takes fewer steps over fewer accumulators (int8:
+  // 16 codes a lane took three steps over 64; bf16: two over 32 became one
+  // over 16; 9B-shaped 4-bit stack 486.6 -> 489.8, 1B-shaped 1685 -> 1694.5
+  // tok/s, same box)
+  constexpr bool V8 = I8 || KVT == 1;        // value rows in 8-byte lane loads
+  constexpr int VDPL8 = I8 ? 8 : 4;           // dims per 8-byte load
+  constexpr int VLPR = V8 ? D / VDPL8 : LPR;  // lanes per value row
   constexpr int VRPS = (kWave / VLPR) * kWaves;  // value rows per workgroup step
   const int vsub = lane / VLPR;
-  const int vd0 = (lane % VLPR) * 8;          // int8: first code of the lane
-  const int nvsteps = I8 ? (tl - t0 + VRPS - 1) / VRPS : nsteps;
+  const int vd0 = (lane % VLPR) * VDPL8;      // first dim of the lane (8-byte loads)
+  const int nvsteps = V8 ? (tl - t0 + VRPS - 1) / VRPS : nsteps;
   auto vrow8 = [&](int step) { return t0 + step * VRPS + wv * (kWave / VLPR) + vsub; };
-  uint2 v8[I8 ? U : 1];
+  uint2 v8[V8 ? U : 1];
   auto load_v8 = [&](int step, int u) {
     const int t = vrow8(step);
     const bool ok = step < nvsteps && t < tl;
-    v8[u] = ok ? *reinterpret_cast<const uint2*>(vb + size_t(t) * D + vd0) : make_uint2(0u, 0u);
+    v8[u] = ok ? *reinterpret_cast<const uint2*>(vb + (size_t(t) * D + vd0) * EB) : make_uint2(0u, 0u);
   };
 
   // first batch of K rows, of V rows (VLATE: once the scores are done),
   // then the queries
-  u32x4 kv[U], vv[I8 ? 1 : U];
+  u32x4 kv[U], vv[V8 ? 1 : U];
   auto first_v = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if constexpr (I8) {
+      if constexpr (V8) {
         load_v8(u, u);
       } else {
         const int t = row(u);
@@ -260,12 +265,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   __syncthreads();
 
   // ---- o = sum_t p_t v_t
-  if constexpr (I8) {
-    float o8[G][8];
+  if constexpr (V8) {
+    float o8[G][VDPL8];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o8[hh][e] = 0.0f;
+      for (int e = 0; e < VDPL8; ++e) o8[hh][e] = 0.0f;
     for (int b = 0; b < nvsteps; b += U) {
       if (b > 0) {
 #pragma unroll
@@ -275,17 +280,21 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       for (int u = 0; u < U; ++u) {
         const int t = vrow8(b + u);
         if (b + u < nvsteps && t < tl) {
-          float vf[8];
+          float vf[VDPL8];
+          if constexpr (I8) {
 #pragma unroll
-          for (int bi = 0; bi < 4; ++bi) {
-            vf[bi] = float(int8_t(uint8_t(v8[u].x >> (8 * bi))));
-            vf[4 + bi] = float(int8_t(uint8_t(v8[u].y >> (8 * bi))));
+            for (int bi = 0; bi < 4; ++bi) {
+              vf[bi] = float(int8_t(uint8_t(v8[u].x >> (8 * bi))));
+              vf[4 + bi] = float(int8_t(uint8_t(v8[u].y >> (8 * bi))));
+            }
+          } else {
+            vf[0] = bf_lo(v8[u].x); vf[1] = bf_hi(v8[u].x); vf[2] = bf_lo(v8[u].y); vf[3] = bf_hi(v8[u].y);
           }
 #pragma unroll
           for (int hh = 0; hh < G; ++hh) {
             const float p = sc[hh][t - t0];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o8[hh][e] = fmaf(p, vf[e], o8[hh][e]);
+            for (int e = 0; e < VDPL8; ++e) o8[hh][e] = fmaf(p, vf[e], o8[hh][e]);
           }
         }
       }
@@ -293,12 +302,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o8[hh][e] = fold_groups<VLPR>(o8[hh][e]);
+      for (int e = 0; e < VDPL8; ++e) o8[hh][e] = fold_groups<VLPR>(o8[hh][e]);
     if (vsub == 0)
 #pragma unroll
       for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ored[wv][hh][vd0 + e] = o8[hh][e];
+        for (int e = 0; e < VDPL8; ++e) ored[wv][hh][vd0 + e] = o8[hh][e];
   } else {
   float o[G][DPL];
 #pragma unroll
