@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define DEC_ABI_VERSION 6
+#define DEC_ABI_VERSION 7
 
 enum dec_dtype { DEC_F32 = 0, DEC_BF16 = 1, DEC_Q4 = 2, DEC_I8 = 3 };
 
@@ -131,6 +131,12 @@ enum dec_status {
                                        (at p when p + 1 is past the cache) */
 #define DEC_TEST_DROP_SPLIT 0x800u  /* attention combines leave out the last split
                                        (when there are two or more) */
+/* Debugging: the QKV step (fused or per-op) also writes the token's rotated
+   k and plain v rows as float32, before they are rounded to the cache type,
+   to st->scratch from float offset dec_scratch_kv_offset(desc): k [n_kv][d],
+   then v [n_kv][d]. A test can then check every appended cache value
+   against its own float32 source bit for bit. Needs st->scratch. */
+#define DEC_DEBUG_EXPORT_KV 0x80u
 
 /* Static shape of one decoder layer (identical for every layer of a stack). */
 typedef struct {
@@ -191,8 +197,8 @@ typedef struct {
   const float* rope;   /* [max_ctx][d/2][2] (cos, sin) from dec_rope_table */
   uint32_t* err;       /* device error word (bits are OR-ed in) */
   float* scratch;      /* [dec_scratch_floats(desc)]; used by DEC_UNFUSED,
-                          DEC_NO_FUSE_QKV and DEC_NO_FUSE_FFN only, may be
-                          NULL otherwise */
+                          DEC_NO_FUSE_QKV, DEC_NO_FUSE_FFN and
+                          DEC_DEBUG_EXPORT_KV only, may be NULL otherwise */
 } dec_layer_state;
 
 /* ---- sizes of caller-provided buffers ---------------------------------- */
@@ -211,8 +217,12 @@ int64_t dec_attn_part_floats(const dec_layer_desc* desc);
 int64_t dec_cache_bytes(const dec_layer_desc* desc);
 int64_t dec_cache_scale_offset(const dec_layer_desc* desc);
 int64_t dec_cache_stage_offset(const dec_layer_desc* desc);
-/* floats needed by dec_layer_state.scratch for the per-op path. */
+/* floats needed by dec_layer_state.scratch for the per-op path (with
+   DEC_DEBUG_EXPORT_KV in desc->flags, also for the exported k and v rows). */
 int64_t dec_scratch_floats(const dec_layer_desc* desc);
+/* float offset in st->scratch of the rows DEC_DEBUG_EXPORT_KV writes (after
+   every per-op intermediate, so a layer step does not overwrite them). */
+int64_t dec_scratch_kv_offset(const dec_layer_desc* desc);
 
 /* ---- the five kernels of a fused layer -------------------------------- */
 
@@ -355,7 +365,8 @@ int dec_layer_step(const dec_layer_desc* desc, const dec_layer_weights* w,
    the counters on `stream`; nothing is allocated, copied or synchronized.
    Every call on one GPU shares that GPU's array, which keeps the last call's
    contents, so calls that overlap on one GPU (other streams, other threads)
-   race and must be serialized by the caller. */
+   race and must be serialized by the caller. DEC_DEBUG_EXPORT_KV is
+   refused (DEC_E_UNSUPPORTED): its rows would land in the static array. */
 int dec_layer_step_static(const dec_layer_desc* desc, const dec_layer_weights* w,
                           const dec_layer_state* st, void* stream);
 

@@ -90,7 +90,7 @@ int main(void) {
          DEC_NO_FUSE_FFN, DEC_NO_FUSE_ATTN_O);
   printf("DEC_DETERMINISTIC value %u\nDEC_TEST_SKIP_ROPE value %u\nDEC_TEST_APPEND_NEXT value %u\n",
          DEC_DETERMINISTIC, DEC_TEST_SKIP_ROPE, DEC_TEST_APPEND_NEXT);
-  printf("DEC_FUSE_DOWN value %u\n", DEC_FUSE_DOWN);
+  printf("DEC_FUSE_DOWN value %u\nDEC_DEBUG_EXPORT_KV value %u\n", DEC_FUSE_DOWN, DEC_DEBUG_EXPORT_KV);
   printf("DEC_TEST_DROP_SPLIT value %u\nDEC_E_UNSUPPORTED value %d\n", DEC_TEST_DROP_SPLIT, DEC_E_UNSUPPORTED);
   printf("DEC_ERR_POS value %u\nDEC_ERR_TOKEN value %u\nDEC_ERR_SYNC value %u\n", DEC_ERR_POS, DEC_ERR_TOKEN,
          DEC_ERR_SYNC);
@@ -120,7 +120,7 @@ def test_struct_layout_matches_a_c_compiler(L, tmp_path):
                     "DEC_TEST_NO_WAIT": L.DEC_TEST_NO_WAIT, "DEC_NO_FUSE_QKV": L.DEC_NO_FUSE_QKV,
                     "DEC_NO_FUSE_FFN": L.DEC_NO_FUSE_FFN, "DEC_NO_FUSE_ATTN_O": L.DEC_NO_FUSE_ATTN_O,
                     "DEC_DETERMINISTIC": L.DEC_DETERMINISTIC, "DEC_TEST_SKIP_ROPE": L.DEC_TEST_SKIP_ROPE,
-                    "DEC_FUSE_DOWN": L.DEC_FUSE_DOWN,
+                    "DEC_FUSE_DOWN": L.DEC_FUSE_DOWN, "DEC_DEBUG_EXPORT_KV": L.DEC_DEBUG_EXPORT_KV,
                     "DEC_TEST_APPEND_NEXT": L.DEC_TEST_APPEND_NEXT, "DEC_TEST_DROP_SPLIT": L.DEC_TEST_DROP_SPLIT,
                     "DEC_E_UNSUPPORTED": E_UNSUPPORTED,
                     "DEC_ERR_POS": L.DEC_ERR_POS, "DEC_ERR_TOKEN": L.DEC_ERR_TOKEN, "DEC_ERR_SYNC": L.DEC_ERR_SYNC,
@@ -132,7 +132,7 @@ def test_struct_layout_matches_a_c_compiler(L, tmp_path):
         else:
             assert getattr(getattr(L, name), field).offset == val, f"{name}.{field}"
         seen += 1
-    assert seen == 61   # 4 sizes, 33 offsets, 24 constants
+    assert seen == 62   # 4 sizes, 33 offsets, 25 constants
 
 
 # ---- host-side checks (every call below is rejected before any launch)
@@ -305,10 +305,32 @@ def test_null_arguments_are_rejected(L):
     assert lib.dec_advance(None, 0, 8, None, None, None) == E_NULL
 
 
-@pytest.mark.parametrize("flag", ["DEC_UNFUSED", "DEC_NO_FUSE_QKV", "DEC_NO_FUSE_FFN"])
+@pytest.mark.parametrize("flag", ["DEC_UNFUSED", "DEC_NO_FUSE_QKV", "DEC_NO_FUSE_FFN", "DEC_DEBUG_EXPORT_KV"])
 def test_per_op_paths_need_scratch(L, flag):
     d = desc_of(L, synth.CONFIGS["C4"], flags=getattr(L, flag))
     assert rc_step(L, d, weights_of(L), state_of(L)) == E_NULL and "scratch" in L.dec_last_error()
+
+
+def test_debug_kv_export_sits_after_the_per_op_intermediates(L):
+    """DEC_DEBUG_EXPORT_KV: the k and v rows (2 n_kv d floats) follow every
+    per-op intermediate in the scratch buffer, which grows by that much; the
+    QKV entry point then needs scratch too, and the static step refuses the
+    flag (its scratch is the library's own)."""
+    lib = L.load()
+    cfg = synth.CONFIGS["C4"]
+    p4 = lambda v: (v + 3) // 4 * 4  # noqa: E731
+    plain, dbg = desc_of(L, cfg), desc_of(L, cfg, flags=L.DEC_DEBUG_EXPORT_KV)
+    off = p4(cfg.hidden) + p4(cfg.n_qkv) + 2 * p4(cfg.ffn)
+    assert L.dec_scratch_kv_offset(plain) == L.dec_scratch_kv_offset(dbg) == off
+    assert L.dec_scratch_floats(plain) == off
+    assert L.dec_scratch_floats(dbg) == off + p4(2 * cfg.n_kv_heads * cfg.head_dim)
+    assert lib.dec_rmsnorm_gemv_qkv_rope(ctypes.byref(dbg), ctypes.byref(weights_of(L)),
+                                         ctypes.byref(state_of(L)), None) == E_NULL
+    assert "scratch" in L.dec_last_error()
+    st = state_of(L, part=None, counters=None)
+    assert lib.dec_layer_step_static(ctypes.byref(dbg), ctypes.byref(weights_of(L)), ctypes.byref(st),
+                                     None) == E_UNSUPPORTED
+    assert "DEC_DEBUG_EXPORT_KV" in L.dec_last_error()
 
 
 def test_combine_in_output_projection_is_refused_where_it_does_not_apply(L):

@@ -13,6 +13,12 @@ are built so the sums hit values that need that rounding, ties included
 260). The slot's bits must equal the oracle's bit for bit, through the
 fused QKV kernel, through dec_layer_step, and through the per-op path; and
 every other slot keeps its sentinel.
+
+The general case, on random weights at any position (DEC_DEBUG_EXPORT_KV:
+the QKV step also writes its float32 k and v rows before they are rounded):
+every appended cache value is the oracle's rounding of the exported row, bit
+for bit (f32 and bf16 caches; int8 codes and scales from the oracle's
+quantize_i8), and the exported rows match the oracle's float64 k and v.
 """
 import numpy as np
 import pytest
@@ -20,6 +26,7 @@ import torch
 
 import oracle
 import synth
+from helpers import rel_l2
 from transformer_layer_amd import lib as L
 from transformer_layer_amd.engine import DecodeStack
 
@@ -129,3 +136,58 @@ def test_integer_exact_append_is_bitwise(gpu, wtype, kvtype, route):
     # q is exact too (float32 integers)
     if route == "qkv_kernel":
         assert np.array_equal(st.q.cpu().numpy(), y[:kv0].astype(np.float32))
+
+
+EXPORT_CASES = {
+    # the 9B-shaped layer's QKV step (bf16 weights), and small ragged shapes
+    "9b_bf16": lambda kv: synth.CONFIGS["C4"].with_(kvtype=kv, n_layers=1, ctx=0),
+    "ragged_bf16": lambda kv: synth.tiny(n_layers=1, hidden=1040, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=344,
+                                         wtype="bf16", ntype="bf16", kvtype=kv, htype="bf16", ctx=0, steps=8,
+                                         seed=47),
+    "ragged_q4": lambda kv: synth.tiny(n_layers=1, hidden=1024, n_q_heads=8, n_kv_heads=4, head_dim=128, ffn=384,
+                                       wtype="q4", ntype="f32", kvtype=kv, htype="bf16", ctx=0, steps=8, seed=53),
+}
+
+
+@pytest.mark.parametrize("path", ["fused", "per-op"])
+@pytest.mark.parametrize("kvtype", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("case", list(EXPORT_CASES))
+def test_every_appended_value_is_its_exported_row_rounded(gpu, case, kvtype, path):
+    cfg = EXPORT_CASES[case](kvtype)
+    flags = L.DEC_DEBUG_EXPORT_KV | (L.DEC_UNFUSED if path == "per-op" else 0)
+    st = DecodeStack(cfg, n_layers=1, flags=flags)
+    lw = synth.layer_weights(cfg, 0)
+    st.set_layer(0, lw)
+    embed = synth.embedding(cfg)
+    st.set_embedding(embed)
+    o = oracle.Oracle(cfg, [lw], glob={"embed": embed})
+    off, nkv, d = L.dec_scratch_kv_offset(st.desc), cfg.n_kv_heads, cfg.head_dim
+    toks = synth.tokens(cfg)
+    for i, p in enumerate(sorted({0, 1, 2, cfg.max_ctx // 2 + 1, cfg.max_ctx - 1})):
+        st.scratch.fill_(float("nan"))
+        st.set_pos(p)
+        st.set_token(int(toks[i]))
+        st.token_step()
+        torch.cuda.synchronize()
+        assert st.check_err() == 0
+        ex = st.scratch[off: off + 2 * nkv * d].cpu().numpy().reshape(2, nkv, d)
+        assert not np.isnan(ex).any(), "export incomplete"
+        # the exported rows against the oracle's float64 k and v
+        u = oracle.rmsnorm(o.embed(int(toks[i])), o.w(0, "attn_norm"), cfg.rms_eps)
+        y = o.proj(0, "wqkv", u)
+        k = oracle.rope(y[cfg.q_dim: cfg.q_dim + cfg.kv_dim].reshape(nkv, d), p, cfg.rope_theta)
+        v = y[cfg.q_dim + cfg.kv_dim:].reshape(nkv, d)
+        assert rel_l2(ex[0], k) <= 1e-5 and rel_l2(ex[1], v) <= 1e-5, f"position {p}"
+        # every appended value is the rounding of its exported float32
+        for src, cache, sc in ((ex[0], st.K, getattr(st, "Ks", None)), (ex[1], st.V, getattr(st, "Vs", None))):
+            got = cache[0, :, p].cpu()
+            if kvtype == "f32":
+                assert np.array_equal(got.numpy().view(np.uint32), src.view(np.uint32)), f"position {p}"
+            elif kvtype == "bf16":
+                assert np.array_equal(got.view(torch.int16).numpy().view(np.uint16),
+                                      oracle.round_to_cache(src, "bf16")), f"position {p}"
+            else:
+                codes, scales = oracle.quantize_i8(src)
+                assert np.array_equal(got.numpy(), codes), f"position {p}: codes"
+                assert np.array_equal(sc[0, :, p].cpu().numpy().view(np.uint32), scales.view(np.uint32)), \
+                    f"position {p}: scales"

@@ -110,9 +110,21 @@ dec::GemvArgs base_args(const dec_layer_desc* d) {
   return a;
 }
 
+// Float offset of the DEC_DEBUG_EXPORT_KV rows in the scratch buffer: after
+// the per-op path's u, y, and the two FFN vectors.
+int64_t kv_export_off(const dec_layer_desc* d) {
+  const int64_t nqkv = int64_t(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+  return pad4(d->hidden) + pad4(nqkv) + 2 * pad4(d->ffn);
+}
+
+float* kv_export(const dec_layer_desc* d, const dec_layer_state* st) {
+  return (d->flags & DEC_DEBUG_EXPORT_KV) ? st->scratch + kv_export_off(d) : nullptr;
+}
+
 int qkv_launch(const dec_layer_desc* d, const dec_layer_weights* w, const dec_layer_state* st,
                hipStream_t s) {
   dec::GemvArgs a = base_args(d);
+  a.dbg_kv = kv_export(d, st);
   a.W = w->wqkv.w;
   a.S = w->wqkv.scales;
   a.rows = (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
@@ -295,7 +307,7 @@ int qkv_unfused(const dec_layer_desc* d, const dec_layer_weights* w, const dec_l
   if ((rc = launched(gemv(d->wtype, dec::kEpiStore, a, s), "gemv_qkv"))) return rc;
   return launched(dec::launch_rope_append(y, st->q, st->k_cache, st->v_cache, st->pos, st->rope, st->err,
                                           d->n_q_heads, d->n_kv_heads, d->head_dim, d->max_ctx,
-                                          kv_kind(d), nullk, s),
+                                          kv_kind(d), kv_export(d, st), nullk, s),
                   "rope_append");
 }
 
@@ -333,7 +345,8 @@ int check_state(const dec_layer_state* st, bool scratch) {
   if (!st->x || !st->q || !st->attn || !st->h || !st->part || !st->counters || !st->k_cache ||
       !st->v_cache || !st->pos || !st->rope || !st->err)
     return fail(DEC_E_NULL, "a state pointer is NULL");
-  if (scratch && !st->scratch) return fail(DEC_E_NULL, "scratch is NULL (needed by DEC_UNFUSED, DEC_NO_FUSE_QKV, DEC_NO_FUSE_FFN)");
+  if (scratch && !st->scratch)
+    return fail(DEC_E_NULL, "scratch is NULL (needed by DEC_UNFUSED, DEC_NO_FUSE_QKV, DEC_NO_FUSE_FFN, DEC_DEBUG_EXPORT_KV)");
   for (const void* p : {(const void*)st->x, (const void*)st->q, (const void*)st->attn,
                         (const void*)st->h, (const void*)st->part, (const void*)st->k_cache,
                         (const void*)st->v_cache})
@@ -437,14 +450,19 @@ int64_t dec_cache_stage_offset(const dec_layer_desc* d) {
 
 int64_t dec_scratch_floats(const dec_layer_desc* d) {
   if (check_desc(d)) return -1;
-  const int64_t nqkv = int64_t(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
-  return pad4(d->hidden) + pad4(nqkv) + 2 * pad4(d->ffn);
+  const int64_t kv = (d->flags & DEC_DEBUG_EXPORT_KV) ? pad4(2 * int64_t(d->n_kv_heads) * d->head_dim) : 0;
+  return kv_export_off(d) + kv;
+}
+
+int64_t dec_scratch_kv_offset(const dec_layer_desc* d) {
+  if (check_desc(d)) return -1;
+  return kv_export_off(d);
 }
 
 int dec_rmsnorm_gemv_qkv_rope(const dec_layer_desc* d, const dec_layer_weights* w,
                               const dec_layer_state* st, void* stream) {
   int rc;
-  if ((rc = check_desc(d)) || (rc = check_state(st, false))) return rc;
+  if ((rc = check_desc(d)) || (rc = check_state(st, (d->flags & DEC_DEBUG_EXPORT_KV) != 0))) return rc;
   if (!w) return fail(DEC_E_NULL, "weights are NULL");
   if (!w->attn_norm) return fail(DEC_E_NULL, "attn_norm is NULL");
   if ((rc = check_mat(d, w->wqkv, "wqkv"))) return rc;
@@ -519,7 +537,8 @@ int dec_layer_step(const dec_layer_desc* d, const dec_layer_weights* w, const de
   const bool split_qkv = f & (DEC_UNFUSED | DEC_NO_FUSE_QKV);
   const bool split_ffn = f & (DEC_UNFUSED | DEC_NO_FUSE_FFN);
   const bool fuse_down = (f & DEC_FUSE_DOWN) && !split_ffn;
-  if ((rc = check_desc(d)) || (rc = check_weights(d, w)) || (rc = check_state(st, split_qkv || split_ffn))) return rc;
+  const bool scratch = split_qkv || split_ffn || (f & DEC_DEBUG_EXPORT_KV);
+  if ((rc = check_desc(d)) || (rc = check_weights(d, w)) || (rc = check_state(st, scratch))) return rc;
   if (fuse_down && (rc = ffn_down_possible(d))) return rc;
   hipStream_t s = hipStream_t(stream);
   const int H = d->hidden, F = d->ffn, qd = d->n_q_heads * d->head_dim;
@@ -542,6 +561,8 @@ int dec_layer_step_static(const dec_layer_desc* d, const dec_layer_weights* w, c
   int rc;
   if ((rc = check_desc(d))) return rc;
   if (!st) return fail(DEC_E_NULL, "state is NULL");
+  if (d->flags & DEC_DEBUG_EXPORT_KV)
+    return fail(DEC_E_UNSUPPORTED, "DEC_DEBUG_EXPORT_KV writes to st->scratch, which the static step does not use");
   const int64_t part = pad64(dec_attn_part_floats(d));
   const int64_t ops = dec_scratch_floats(d);
   if (int64_t(d->n_kv_heads) * DEC_COUNTER_STRIDE > int64_t(kStaticCounterWords) ||

@@ -177,6 +177,11 @@ struct PairEpi {
       } else {
         const bool isk = head < a.nq + a.nkv;
         const int j = isk ? head - a.nq : head - a.nq - a.nkv;
+        if (a.dbg_kv) {   // the rows before rounding (debug export)
+          float* dk = a.dbg_kv + (isk ? 0 : a.nkv * a.d) + j * a.d + i;
+          dk[0] = y0;
+          dk[half] = y1;
+        }
         const int slot = (a.fault & kFaultAppendNext) && pos + 1 < a.max_ctx ? pos + 1 : pos;
         const size_t off = (size_t(j) * a.max_ctx + slot) * a.d + i;
         void* cache = isk ? a.kc : a.vc;

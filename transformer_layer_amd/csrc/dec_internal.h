@@ -56,6 +56,7 @@ struct GemvArgs {
   uint32_t* err;
   int null_kernel;
   int fault;           // kFault* bits (tests of the parity gates only)
+  float* dbg_kv;       // QKV epilogue: k [nkv][d] then v [nkv][d] as float32 before rounding, or null
 };
 
 // Granules (16-byte weight groups) per lane for a row of `cols` elements
@@ -186,7 +187,7 @@ hipError_t launch_rmsnorm_like(const float* x, const void* g, int ntype, float* 
 hipError_t launch_mul(float* u, const void* g, int ntype, int n, int null_kernel, hipStream_t s);
 hipError_t launch_rope_append(const float* y, float* q, void* kc, void* vc, const int32_t* pos,
                               const float* rope, uint32_t* err, int nq, int nkv, int d, int max_ctx,
-                              int kvtype, int null_kernel, hipStream_t s);
+                              int kvtype, float* dbg_kv, int null_kernel, hipStream_t s);
 hipError_t launch_swiglu(const float* g, const float* u, float* h, int n, int null_kernel,
                          hipStream_t s);
 hipError_t launch_rope_table(double theta, int d, int max_ctx, float* table, hipStream_t s);

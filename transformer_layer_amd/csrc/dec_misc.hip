@@ -73,7 +73,7 @@ __global__ void mul_kernel(float* u, const void* g, int ntype, int n, int null_k
 // RoPE on q and k heads of y = Wqkv u, q written out, k and v appended.
 __global__ void rope_append_kernel(const float* y, float* q, void* kc, void* vc,
                                    const int32_t* pos_p, const float* rope, uint32_t* err, int nq,
-                                   int nkv, int d, int max_ctx, int kvtype, int null_kernel) {
+                                   int nkv, int d, int max_ctx, int kvtype, float* dbg_kv, int null_kernel) {
   if (null_kernel) return;
   const int pos = *pos_p;
   if (pos < 0 || pos >= max_ctx) {
@@ -98,6 +98,11 @@ __global__ void rope_append_kernel(const float* y, float* q, void* kc, void* vc,
   }
   const bool isk = head < nq + nkv;
   const int j = isk ? head - nq : head - nq - nkv;
+  if (dbg_kv) {   // the rows before rounding (debug export)
+    float* dk = dbg_kv + (isk ? 0 : nkv * d) + j * d + i;
+    dk[0] = y0;
+    dk[half] = y1;
+  }
   const size_t off = (size_t(j) * max_ctx + pos) * d + i;
   void* cache = isk ? kc : vc;
   if (kvtype == 2) {   // int8 cache: the row is staged as float, the attention appends it
@@ -203,10 +208,10 @@ hipError_t launch_mul(float* u, const void* g, int ntype, int n, int null_kernel
 
 hipError_t launch_rope_append(const float* y, float* q, void* kc, void* vc, const int32_t* pos,
                               const float* rope, uint32_t* err, int nq, int nkv, int d, int max_ctx,
-                              int kvtype, int null_kernel, hipStream_t s) {
+                              int kvtype, float* dbg_kv, int null_kernel, hipStream_t s) {
   const int n = (nq + 2 * nkv) * d / 2;
   hipLaunchKernelGGL(rope_append_kernel, dim3((n + 255) / 256), dim3(256), 0, s, y, q, kc, vc, pos,
-                     rope, err, nq, nkv, d, max_ctx, kvtype, null_kernel);
+                     rope, err, nq, nkv, d, max_ctx, kvtype, dbg_kv, null_kernel);
   return hipGetLastError();
 }
 

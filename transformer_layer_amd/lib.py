@@ -21,6 +21,7 @@ DEC_NO_FUSE_FFN = 0x8
 DEC_NO_FUSE_ATTN_O = 0x10
 DEC_DETERMINISTIC = 0x20
 DEC_FUSE_DOWN = 0x40
+DEC_DEBUG_EXPORT_KV = 0x80
 DEC_ATTN_KERNEL_MASK = 0x3000
 DEC_ATTN_BATCHED = 0x1000
 DEC_ATTN_STREAM = 0x2000
@@ -32,7 +33,7 @@ DEC_TEST_DROP_SPLIT = 0x800
 DEC_ERR_POS = 0x1
 DEC_ERR_TOKEN = 0x2
 DEC_ERR_SYNC = 0x4
-ABI_VERSION = 6
+ABI_VERSION = 7
 DEC_COUNTER_STRIDE = 16
 DEC_STATIC_SCRATCH_BYTES = 4 << 20
 
@@ -71,6 +72,7 @@ P_ST = ctypes.POINTER(dec_layer_state)
 SIGNATURES = {
     "dec_attn_part_floats": (c_int64, [P_DESC]),
     "dec_scratch_floats": (c_int64, [P_DESC]),
+    "dec_scratch_kv_offset": (c_int64, [P_DESC]),
     "dec_cache_bytes": (c_int64, [P_DESC]),
     "dec_cache_scale_offset": (c_int64, [P_DESC]),
     "dec_cache_stage_offset": (c_int64, [P_DESC]),
@@ -151,6 +153,10 @@ def dec_scratch_floats(desc: dec_layer_desc) -> int:
     if n < 0:
         raise DecError(_lib.dec_last_error().decode())
     return n
+
+
+def dec_scratch_kv_offset(desc: dec_layer_desc) -> int:
+    return _size("dec_scratch_kv_offset", desc)
 
 
 def _size(name: str, desc: dec_layer_desc) -> int:
