@@ -25,10 +25,36 @@
 // x * (127 / max |x|) rounded half to even, all in float32), stores codes and
 // scales into slot p, and scores and sums the token from those codes.
 //
+// A bf16 cache with at most four query heads per kv head scores on the
+// matrix cores (v_mfma_f32_16x16x32_bf16): a 16-row tile of K is the A
+// operand as stored (lane l: row l % 16, dims 32 ks + 8 (l / 16) .. + 7 for
+// step ks), and the B operand's columns hold each query head three times, as
+// three bf16 parts hi + mid + lo of q scaled (column p G + h: part p of head
+// h; the other columns zero). A bf16 x bf16 product is exact in float32 and
+// the three parts keep every bit of q's float32 significand, so a row's
+// score is the float32 dot product up to the order of its additions; two DPP
+// adds sum the three columns of a head. On the vector ALUs each 16 rows cost
+// about 250 instructions a wave (unpacking, products, lane folds), here 4
+// matrix operations and about 10 instructions.
+//
 // Partials, arrival and combine: attn_finish (dec_attn_common.h).
 #include "dec_attn_common.h"
 
 namespace dec {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Part p (0: hi, 1: mid, 2: lo) of x as bf16 bits: hi = bf16(x), mid =
+// bf16(x - hi), lo = bf16(x - hi - mid), each difference exact in float32.
+__device__ __forceinline__ uint32_t q_part_bf16(float x, int p) {
+  const uint16_t hi = f32_to_bf16(x);
+  if (p == 0) return hi;
+  const float r = x - bf16_to_f32(hi);
+  const uint16_t mid = f32_to_bf16(r);
+  if (p == 1) return mid;
+  return f32_to_bf16(r - bf16_to_f32(mid));
+}
 
 template <int D, int KVT, int G, int NW, bool VLATE>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
@@ -42,6 +68,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int RPS = RPW * kWaves;     // rows per workgroup step
   constexpr int U = 8;                  // row steps in flight per batch
   static_assert(LPR >= 2 && LPR <= 32, "row layout");
+  constexpr bool MS = KVT == 1 && 3 * G <= 16 && D % 32 == 0;   // scores on the matrix cores
+  constexpr int KSTEPS = D / 32;         // matrix steps per 16-row tile
+  constexpr int UT = KSTEPS >= 4 ? 2 : 4;   // tiles in flight per wave
+  constexpr int QPAIRS = 16 * D / 2;     // B operand: 16 columns of D bf16, two a word
+  constexpr int QPT = (QPAIRS + kBlock - 1) / kBlock;
 
   if (a.null_kernel) return;
   const int j = blockIdx.x % a.nkv;
@@ -121,9 +152,39 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     v8[u] = ok ? *reinterpret_cast<const uint2*>(vb + (size_t(t) * D + vd0) * EB) : make_uint2(0u, 0u);
   };
 
+  // matrix-core scores: this thread's words of the B operand (q read
+  // first, so that waiting for it does not wait for K), then the wave's
+  // first tiles of K (tiles wv, wv + NW, ...; lane l reads row l % 16)
+  const int nrow = tl - t0;
+  const int ntile = (nrow + 15) / 16;
+  const int kr = lane & 15, kg = lane >> 4;
+  float2 qx[MS ? QPT : 1];
+  u32x4 kt[MS ? UT : 1][MS ? KSTEPS : 1];
+  auto load_tiles = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      const int tile = wv + kWaves * (b + u);
+      const int t = t0 + 16 * tile + kr;
+      const bool ok = tile < ntile && t < tl;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        kt[u][ks] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + 32 * ks + 8 * kg) * EB) : z;
+    }
+  };
+  if constexpr (MS) {
+#pragma unroll
+    for (int r = 0; r < QPT; ++r) {
+      const int e = threadIdx.x + r * kBlock;   // word e: column e / (D / 2), dims 2 (e % (D / 2)) + 0, 1
+      const int c = e / (D / 2), dd = 2 * (e % (D / 2));
+      qx[r] = e < QPAIRS && c < 3 * G ? *reinterpret_cast<const float2*>(a.q + (j * G + c % G) * D + dd)
+                                      : make_float2(0.0f, 0.0f);
+    }
+    load_tiles(0);
+  }
+
   // first batch of K rows, of V rows (VLATE: once the scores are done),
   // then the queries
-  u32x4 kv[U], vv[V8 ? 1 : U];
+  u32x4 kv[MS ? 1 : U], vv[V8 ? 1 : U];
   auto first_v = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -136,25 +197,30 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       }
     }
   };
+  if constexpr (!MS) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int t = row(u);
-    const bool ok = u < nsteps && t < tl;
-    kv[u] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + d0) * EB) : z;
+    for (int u = 0; u < U; ++u) {
+      const int t = row(u);
+      const bool ok = u < nsteps && t < tl;
+      kv[u] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + d0) * EB) : z;
+    }
   }
   if constexpr (!VLATE) first_v();
   const float qscale = kLog2e / sqrtf(float(D));
-  float qv[G][DPL];
+  float qv[MS ? 1 : G][MS ? 1 : DPL];
+  if constexpr (!MS) {
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+    for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-    for (int e = 0; e < DPL; e += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(a.q + (j * G + hh) * D + d0 + e);
-      qv[hh][e] = x.x * qscale; qv[hh][e + 1] = x.y * qscale;
-      qv[hh][e + 2] = x.z * qscale; qv[hh][e + 3] = x.w * qscale;
-    }
+      for (int e = 0; e < DPL; e += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(a.q + (j * G + hh) * D + d0 + e);
+        qv[hh][e] = x.x * qscale; qv[hh][e + 1] = x.y * qscale;
+        qv[hh][e + 2] = x.z * qscale; qv[hh][e + 3] = x.w * qscale;
+      }
+  }
 
-  __shared__ float sc[G][kChunkMax];
+  __shared__ __align__(16) float sc[G][kChunkMax];
+  __shared__ __align__(16) uint32_t qp[MS ? 16 : 1][MS ? D / 2 : 1];   // B operand, column-major words
   __shared__ float stat[G][2];
   __shared__ float ored[kWaves][G][D];
   __shared__ int role;
@@ -163,6 +229,44 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   __shared__ float4 caccs[kBlock];
 
   // ---- scores (log2 units): s_t = (q . k_t) log2(e) / sqrt(d)
+  if constexpr (MS) {
+#pragma unroll
+    for (int r = 0; r < QPT; ++r) {
+      const int e = threadIdx.x + r * kBlock;
+      if (e < QPAIRS) {
+        const int p = (e / (D / 2)) / G;   // 3 and above: a zero column (its q words are zero)
+        qp[e / (D / 2)][e % (D / 2)] = q_part_bf16(qx[r].x * qscale, p) | (q_part_bf16(qx[r].y * qscale, p) << 16);
+      }
+    }
+    __syncthreads();
+    u32x4 qb[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(&qp[kr][16 * ks + 4 * kg]);
+    for (int b = 0; wv + kWaves * b < ntile; b += UT) {
+      if (b > 0) load_tiles(b);
+#pragma unroll
+      for (int u = 0; u < UT; ++u) {
+        const int tile = wv + kWaves * (b + u);   // wave-uniform
+        if (tile < ntile) {
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int ks = 0; ks < KSTEPS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kt[u][ks]),
+                                                          __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
+          // lane kr < G: column kr (rows 4 kg .. 4 kg + 3 of the tile) plus
+          // columns kr + G and kr + 2G (DPP row shifts left by G and 2G)
+          float4 sv;
+          sv.x = acc[0] + dpp_mov<0x100 + G>(acc[0]) + dpp_mov<0x100 + 2 * G>(acc[0]);
+          sv.y = acc[1] + dpp_mov<0x100 + G>(acc[1]) + dpp_mov<0x100 + 2 * G>(acc[1]);
+          sv.z = acc[2] + dpp_mov<0x100 + G>(acc[2]) + dpp_mov<0x100 + 2 * G>(acc[2]);
+          sv.w = acc[3] + dpp_mov<0x100 + G>(acc[3]) + dpp_mov<0x100 + 2 * G>(acc[3]);
+          // rows past the chunk score 0 and are never read; the index stays
+          // below kChunkMax (16 ceil(n / 16) <= kChunkMax)
+          if (kr < G) *reinterpret_cast<float4*>(&sc[kr][16 * tile + 4 * kg]) = sv;
+        }
+      }
+    }
+  } else
   for (int b = 0; b < nsteps; b += U) {
     if (b > 0) {
 #pragma unroll
