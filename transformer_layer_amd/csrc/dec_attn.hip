@@ -42,20 +42,6 @@
 
 namespace dec {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Part p (0: hi, 1: mid, 2: lo) of x as bf16 bits: hi = bf16(x), mid =
-// bf16(x - hi), lo = bf16(x - hi - mid), each difference exact in float32.
-__device__ __forceinline__ uint32_t q_part_bf16(float x, int p) {
-  const uint16_t hi = f32_to_bf16(x);
-  if (p == 0) return hi;
-  const float r = x - bf16_to_f32(hi);
-  const uint16_t mid = f32_to_bf16(r);
-  if (p == 1) return mid;
-  return f32_to_bf16(r - bf16_to_f32(mid));
-}
-
 template <int D, int KVT, int G, int NW, bool VLATE>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int kWaves = NW;        // waves per workgroup (4 or 8)

@@ -20,6 +20,21 @@
 namespace dec {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Part p (0: hi, 1: mid, 2: lo) of x as bf16 bits, for query operands of
+// the matrix cores: hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi -
+// mid), each difference exact in float32; hi + mid + lo holds x's 24-bit
+// significand. Any other p gives lo as well.
+__device__ __forceinline__ uint32_t q_part_bf16(float x, int p) {
+  const uint16_t hi = f32_to_bf16(x);
+  if (p == 0) return hi;
+  const float r = x - bf16_to_f32(hi);
+  const uint16_t mid = f32_to_bf16(r);
+  if (p == 1) return mid;
+  return f32_to_bf16(r - bf16_to_f32(mid));
+}
 
 constexpr int kChunkMax = 256;  // cache positions per split
 constexpr int kSplitMax = 256;  // splits per kv head

@@ -27,6 +27,14 @@
 // its value codes into the LDS row the cache would have filled, so the
 // softmax and the sum treat it like any other row.
 //
+// A bf16 cache with at most four query heads per kv head scores on the
+// matrix cores, as the batched kernel does (its header gives the operand
+// layout): each key wave takes 16-row tiles (wave hw: tiles hw, hw + 4, ...;
+// lane l reads row l % 16), its ring slots holding the tiles' 16-byte steps.
+// The B operand (three bf16 parts of each scaled query head) is built by all
+// eight waves, before any row arrives, in the per-wave output sums' LDS,
+// which stays unused until the sum of p * v.
+//
 // LDS layout (bytes), rows padded to cpad (a whole number of eight-wave
 // row steps): [values cpad x row][scores G x cpad f32][per-wave output sums
 // NW x G x D f32][combine scratch][(m, l) G x 2 f32][role][int8: key and
@@ -91,6 +99,12 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
   const int sub = lane / LPR;
   const int li = lane % LPR;
   const int d0 = li * DPL;
+  constexpr bool MS = KVT == 1 && 3 * G <= 16 && D % 32 == 0;   // scores on the matrix cores
+  constexpr int KSTEPS = D / 32;        // matrix steps (ring slots) per 16-row tile
+  static_assert(!MS || U % KSTEPS == 0, "whole tiles per ring");
+  constexpr int QPAIRS = 16 * D / 2;    // B operand words
+  constexpr int QPT = (QPAIRS + NW * 64 - 1) / (NW * 64);
+  const int kr = lane & 15, kg = lane >> 4;
 
   uint8_t* vbuf = smem;                                                   // [cpad][RB]
   float* sc = reinterpret_cast<float*>(smem + cpad * RB);                 // [G][cpad]
@@ -118,13 +132,34 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
     r = r < nc ? r : rlast;   // every load is issued: past the chunk, its last row again
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + size_t(r) * RB));
   };
+  // matrix-core key waves: slot k holds step k % KSTEPS of the wave's tile
+  // k / KSTEPS (chunk tile hw + 4 (k / KSTEPS)), row kr, dims 32 step + 8 kg
+  const uint8_t* ksrc = reinterpret_cast<const uint8_t*>(a.kc) + (size_t(j) * a.max_ctx + t0) * RB;
+  auto kload = [&](int k) {
+    int r = 16 * (hw + 4 * (k / KSTEPS)) + kr;
+    r = r < nc ? r : rlast;
+    return __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(ksrc + size_t(r) * RB + (32 * (k % KSTEPS) + 8 * kg) * 2));
+  };
+  // the B operand's words of this thread: q first, so waiting for it does
+  // not wait for the ring
+  float2 qx[MS ? QPT : 1];
+  if constexpr (MS) {
+#pragma unroll
+    for (int r = 0; r < QPT; ++r) {
+      const int e = tid + r * NW * 64;   // word e: column e / (D / 2), dims 2 (e % (D / 2)) + 0, 1
+      const int c = e / (D / 2), dd = 2 * (e % (D / 2));
+      qx[r] = e < QPAIRS && c < 3 * G ? *reinterpret_cast<const float2*>(a.q + (j * G + c % G) * D + dd)
+                                      : make_float2(0.0f, 0.0f);
+    }
+  }
   // the ring: slot u holds step k0 + u; a consumed slot is refilled at once
   // with the step U ahead. Every load is issued (a step past the chunk
   // re-reads its last row, a cache hit): refilled conditionally, the
   // compiler waited for the whole ring before each use.
   u32x4 ring[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) ring[u] = load(u);
+  for (int u = 0; u < U; ++u) ring[u] = MS && keys ? kload(u) : load(u);
 
   // int8: the key waves request the chunk's row scales (rows hw * 64 + lane
   // + 256 k, clamped to the streamed rows; written to LDS once the scores
@@ -155,7 +190,53 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
     }
   }
 
-  if (keys) {
+  uint32_t* qp = reinterpret_cast<uint32_t*>(ored);   // [16][D / 2] words; 16 D 2 <= NW G D 4 bytes
+  if constexpr (MS) {
+    const float qscale = kLog2e / sqrtf(float(D));
+#pragma unroll
+    for (int r = 0; r < QPT; ++r) {
+      const int e = tid + r * NW * 64;
+      if (e < QPAIRS) {
+        const int p = (e / (D / 2)) / G;   // 3 and above: a zero column (its q words are zero)
+        qp[e] = q_part_bf16(qx[r].x * qscale, p) | (q_part_bf16(qx[r].y * qscale, p) << 16);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (MS && keys) {
+    // ---- scores (log2 units) on the matrix cores, 16-row tiles
+    u32x4 qb[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(qp + kr * (D / 2) + 16 * ks + 4 * kg);
+    const int ntile = (nc + 15) / 16;
+    const int nk = hw < ntile ? (ntile - hw + 3) / 4 * KSTEPS : 0;   // slots this wave consumes
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < nk; k0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const u32x4 w = ring[u];
+        ring[u] = kload(k0 + U + u);
+        if (k0 + u < nk) {   // wave-uniform
+          const int ks = u % KSTEPS;
+          if (ks == 0) acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
+                                                        __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
+          if (ks == KSTEPS - 1) {
+            // lane kr < G: head kr's three columns (DPP row shifts left by G, 2G)
+            float4 sv;
+            sv.x = acc[0] + dpp_mov<0x100 + G>(acc[0]) + dpp_mov<0x100 + 2 * G>(acc[0]);
+            sv.y = acc[1] + dpp_mov<0x100 + G>(acc[1]) + dpp_mov<0x100 + 2 * G>(acc[1]);
+            sv.z = acc[2] + dpp_mov<0x100 + G>(acc[2]) + dpp_mov<0x100 + 2 * G>(acc[2]);
+            sv.w = acc[3] + dpp_mov<0x100 + G>(acc[3]) + dpp_mov<0x100 + 2 * G>(acc[3]);
+            // rows 16 tile + 4 kg .. + 3 (past nc: never read); 16 ceil(nc / 16) <= cpad
+            const int tile = hw + 4 * ((k0 + u) / KSTEPS);
+            if (kr < G) *reinterpret_cast<float4*>(sc + kr * cpad + 16 * tile + 4 * kg) = sv;
+          }
+        }
+      }
+    }
+  } else if (keys) {
     const float qscale = kLog2e / sqrtf(float(D));
     float qv[G][DPL];
 #pragma unroll
