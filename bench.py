@@ -391,6 +391,8 @@ def main() -> int:
     ap.add_argument("--fuse-down", action="store_true",
                     help="4-bit weights: the gated FFN and the down projection as one kernel (four per layer)")
     ap.add_argument("--attn-chunk", type=int, default=0)
+    ap.add_argument("--attn-kernel", choices=["auto", "batched", "stream", "local"], default="auto",
+                    help="attention kernel (default: the library's choice for the shape)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip the greedy (LM head) timing")
     ap.add_argument("--repeats", type=int, default=5,
@@ -420,7 +422,9 @@ def main() -> int:
         print(json.dumps({"config": cfg.name, "steps": args.steps, "ab": res}), flush=True)
         return 0
     flags = ((L.DEC_UNFUSED if args.unfused else 0) | (L.DEC_NULL_KERNELS if args.null_kernels else 0)
-             | (L.DEC_FUSE_DOWN if args.fuse_down else 0))
+             | (L.DEC_FUSE_DOWN if args.fuse_down else 0)
+             | {"auto": 0, "batched": L.DEC_ATTN_BATCHED, "stream": L.DEC_ATTN_STREAM,
+                "local": L.DEC_ATTN_LOCAL}[args.attn_kernel])
     log(f"config {cfg.name}: building stack ({cfg.n_layers} layers)")
     w = Workload(cfg, flags, args.attn_chunk, eager=args.eager)
     st = w.st
@@ -493,7 +497,8 @@ def main() -> int:
                    "context": cfg.ctx, "decode_window": cfg.steps, "batch": 1,
                    "mode": ("unfused" if args.unfused else "fused") + ("-down" if args.fuse_down else "")
                            + ("-eager" if args.eager else "-graph") + ("-null" if args.null_kernels else ""),
-                   "kernels_per_layer": 10 if args.unfused else 4 if args.fuse_down else 5},
+                   "kernels_per_layer": 10 if args.unfused else 4 if args.fuse_down else 5,
+                   "attention": args.attn_kernel, "attn_chunk": args.attn_chunk or "auto"},
         "bytes_per_token": int(bpt),
         "hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),

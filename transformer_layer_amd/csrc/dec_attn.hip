@@ -59,6 +59,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int UT = KSTEPS >= 4 ? 2 : 4;   // tiles in flight per wave
   constexpr int QPAIRS = 16 * D / 2;     // B operand: 16 columns of D bf16, two a word
   constexpr int QPT = (QPAIRS + kBlock - 1) / kBlock;
+  // value loads in flight per lane: with matrix-core scores the wait for
+  // a second batch of values is no longer hidden, so 128-wide rows keep a
+  // whole default chunk (96 rows) in flight (9B-shaped 4-bit stack 500.2 ->
+  // 509.7 tok/s; 64-wide rows lost 0.6% and keep 8)
+  constexpr int UV = MS && D == 128 ? 12 : U;
 
   if (a.null_kernel) return;
   const int j = blockIdx.x % a.nkv;
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int vd0 = (lane % VLPR) * VDPL8;      // first dim of the lane (8-byte loads)
   const int nvsteps = V8 ? (tl - t0 + VRPS - 1) / VRPS : nsteps;
   auto vrow8 = [&](int step) { return t0 + step * VRPS + wv * (kWave / VLPR) + vsub; };
-  uint2 v8[V8 ? U : 1];
+  uint2 v8[V8 ? UV : 1];
   auto load_v8 = [&](int step, int u) {
     const int t = vrow8(step);
     const bool ok = step < nvsteps && t < tl;
@@ -172,11 +177,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   // then the queries
   u32x4 kv[MS ? 1 : U], vv[V8 ? 1 : U];
   auto first_v = [&]() {
+    if constexpr (V8) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if constexpr (V8) {
-        load_v8(u, u);
-      } else {
+      for (int u = 0; u < UV; ++u) load_v8(u, u);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
         const int t = row(u);
         const bool ok = u < nsteps && t < tl;
         vv[u] = ok ? *reinterpret_cast<const u32x4*>(vb + (size_t(t) * D + d0) * EB) : z;
@@ -361,13 +367,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
       for (int e = 0; e < VDPL8; ++e) o8[hh][e] = 0.0f;
-    for (int b = 0; b < nvsteps; b += U) {
+    for (int b = 0; b < nvsteps; b += UV) {
       if (b > 0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) load_v8(b + u, u);
+        for (int u = 0; u < UV; ++u) load_v8(b + u, u);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < UV; ++u) {
         const int t = vrow8(b + u);
         if (b + u < nvsteps && t < tl) {
           float vf[VDPL8];
