@@ -204,6 +204,8 @@ KERNEL_CASES = [
     (128, 8, 4, 700, (699, 350), 100),            # chunks that end inside a row step
     (64, 8, 8, 1000, (999, 0), 200),
     (128, 32, 8, 4352, (4351,), 0),
+    (128, 16, 4, 300, (0, 1, 16, 17, 299), 16),   # four-head groups (matrix-core scores), one-row splits
+    (64, 4, 2, 333, (332, 5, 32), 33),             # two-head groups, 16-row tiles ending inside a chunk
 ]
 
 
@@ -231,6 +233,36 @@ def test_attn_each_kernel(gpu, kernel, d, nq, nkv, max_ctx, positions, chunk):
         ref = oracle.attend(q.astype(np.float64), Kv[:, : p + 1], Vv[:, : p + 1], nq // nkv)
         assert rel_l2(st.attn.cpu().numpy(), ref.reshape(-1)) <= TOL, f"{kernel} pos {p}"
         assert int(st.counters.abs().sum().item()) == 0, "arrival counters not reset"
+    assert st.check_err() == 0
+
+
+@pytest.mark.parametrize("kernel", ["DEC_ATTN_BATCHED", "DEC_ATTN_STREAM"])
+@pytest.mark.parametrize("nq,nkv", [(32, 8), (16, 8), (8, 8)])
+def test_attn_matrix_core_scores_keep_the_float32_query(gpu, kernel, nq, nkv):
+    """bf16 caches with up to four query heads per kv head score on the
+    matrix cores with the query as three bf16 parts. Queries eight times
+    larger than usual make the softmax sharp. On these inputs (measured on
+    the CPU) float32 arithmetic lands within 8e-7 relative L2 of the
+    oracle, while a query kept to two bf16 parts (about 2^-17 of q) lands
+    5e-6 to 2e-5 away and one part 3e-3 to 1e-2: the bound is 3e-6."""
+    d, max_ctx = 128, 1000
+    cfg = synth.tiny(hidden=256, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, ffn=256, wtype="bf16",
+                     ntype="bf16", kvtype="bf16", ctx=0, steps=max_ctx, seed=12)
+    st = DecodeStack(cfg, n_layers=1, flags=getattr(L, kernel))
+    std = 0.02 * np.sqrt(4096)
+    K = synth.rand_cache((12, 1, max_ctx), nkv, max_ctx, d, "bf16", std)
+    V = synth.rand_cache((12, 2, max_ctx), nkv, max_ctx, d, "bf16", std)
+    st.set_prefill(0, K, V)
+    Kv = oracle.ref.cache_values(K.data, "bf16", np.float64)
+    Vv = oracle.ref.cache_values(V.data, "bf16", np.float64)
+    for i, p in enumerate((999, 500)):
+        q = synth.rand_f32((12, 3, i), (nq, d), std=8 * std)
+        st.q.copy_(torch.from_numpy(q.reshape(-1)))
+        st.set_pos(p)
+        L.dec_attn_splitk(st.desc, st.state[0])
+        torch.cuda.synchronize()
+        ref = oracle.attend(q.astype(np.float64), Kv[:, : p + 1], Vv[:, : p + 1], nq // nkv)
+        assert rel_l2(st.attn.cpu().numpy(), ref.reshape(-1)) <= 3e-6, f"{kernel} pos {p}"
     assert st.check_err() == 0
 
 
