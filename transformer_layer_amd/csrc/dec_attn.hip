@@ -54,8 +54,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int RPS = RPW * kWaves;     // rows per workgroup step
   constexpr int U = 8;                  // row steps in flight per batch
   static_assert(LPR >= 2 && LPR <= 32, "row layout");
-  constexpr bool MS = KVT == 1 && 3 * G <= 16 && D % 32 == 0;   // scores on the matrix cores
-  constexpr int KSTEPS = D / 32;         // matrix steps per 16-row tile
+  // scores on the matrix cores: bf16 caches (three bf16 parts of q) and
+  // int8 caches (three int8 digits of q)
+  constexpr bool MSB = KVT == 1 && 3 * G <= 16 && D % 32 == 0;
+  constexpr bool MSI = KVT == 2 && 3 * G <= 16 && D == 128;
+  constexpr bool MS = MSB || MSI;
+  constexpr int KPS = MSI ? 64 : 32;     // dims per matrix step
+  constexpr int KSTEPS = D / KPS;        // matrix steps per 16-row tile
   constexpr int UT = KSTEPS >= 4 ? 2 : 4;   // tiles in flight per wave
   constexpr int QPAIRS = 16 * D / 2;     // B operand: 16 columns of D bf16, two a word
   constexpr int QPT = (QPAIRS + kBlock - 1) / kBlock;
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   // a second batch of values is no longer hidden, so 128-wide rows keep a
   // whole default chunk (96 rows) in flight (9B-shaped 4-bit stack 500.2 ->
   // 509.7 tok/s; 64-wide rows lost 0.6% and keep 8)
-  constexpr int UV = MS && D == 128 ? 12 : U;
+  constexpr int UV = MSB && D == 128 ? 12 : U;
 
   if (a.null_kernel) return;
   const int j = blockIdx.x % a.nkv;
@@ -149,7 +154,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int nrow = tl - t0;
   const int ntile = (nrow + 15) / 16;
   const int kr = lane & 15, kg = lane >> 4;
-  float2 qx[MS ? QPT : 1];
+  float2 qx[MSB ? QPT : 1];
+  float2 qi = {0.0f, 0.0f};   // int8: wave wv < G holds dims 2 lane, 2 lane + 1 of head wv
   u32x4 kt[MS ? UT : 1][MS ? KSTEPS : 1];
   auto load_tiles = [&](int b) {
 #pragma unroll
@@ -159,10 +165,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       const bool ok = tile < ntile && t < tl;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
-        kt[u][ks] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + 32 * ks + 8 * kg) * EB) : z;
+        kt[u][ks] = ok ? *reinterpret_cast<const u32x4*>(kb + (size_t(t) * D + KPS * ks + KPS / 4 * kg) * EB) : z;
     }
   };
-  if constexpr (MS) {
+  if constexpr (MSB) {
 #pragma unroll
     for (int r = 0; r < QPT; ++r) {
       const int e = threadIdx.x + r * kBlock;   // word e: column e / (D / 2), dims 2 (e % (D / 2)) + 0, 1
@@ -170,8 +176,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       qx[r] = e < QPAIRS && c < 3 * G ? *reinterpret_cast<const float2*>(a.q + (j * G + c % G) * D + dd)
                                       : make_float2(0.0f, 0.0f);
     }
-    load_tiles(0);
   }
+  if constexpr (MSI) {
+    if (wv < G) qi = *reinterpret_cast<const float2*>(a.q + (j * G + wv) * D + 2 * lane);
+  }
+  if constexpr (MS) load_tiles(0);
 
   // first batch of K rows, of V rows (VLATE: once the scores are done),
   // then the queries
@@ -213,6 +222,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 
   __shared__ __align__(16) float sc[G][kChunkMax];
   __shared__ __align__(16) uint32_t qp[MS ? 16 : 1][MS ? D / 2 : 1];   // B operand, column-major words
+  __shared__ int qe[MSI ? G : 1];   // int8: each head's exponent E
   __shared__ float stat[G][2];
   __shared__ float ored[kWaves][G][D];
   __shared__ int role;
@@ -222,39 +232,81 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 
   // ---- scores (log2 units): s_t = (q . k_t) log2(e) / sqrt(d)
   if constexpr (MS) {
+    if constexpr (MSB) {
 #pragma unroll
-    for (int r = 0; r < QPT; ++r) {
-      const int e = threadIdx.x + r * kBlock;
-      if (e < QPAIRS) {
-        const int p = (e / (D / 2)) / G;   // 3 and above: a zero column (its q words are zero)
-        qp[e / (D / 2)][e % (D / 2)] = q_part_bf16(qx[r].x * qscale, p) | (q_part_bf16(qx[r].y * qscale, p) << 16);
+      for (int r = 0; r < QPT; ++r) {
+        const int e = threadIdx.x + r * kBlock;
+        if (e < QPAIRS) {
+          const int p = (e / (D / 2)) / G;   // 3 and above: a zero column (its q words are zero)
+          qp[e / (D / 2)][e % (D / 2)] =
+              q_part_bf16(qx[r].x * qscale, p) | (q_part_bf16(qx[r].y * qscale, p) << 16);
+        }
+      }
+    } else {
+      // int8: wave h < G builds head h's digit columns h, G + h, 2G + h
+      // (column c holds D bytes; columns 3G and up are never read)
+      if (wv < G) {
+        const float x0 = qi.x * qscale, x1 = qi.y * qscale;
+        const int e = query_exp_i8(wave_max(fmaxf(fabsf(x0), fabsf(x1))));
+        int a0, a1, a2, b0, b1, b2;
+        query_digits_i8(x0, e, a0, a1, a2);
+        query_digits_i8(x1, e, b0, b1, b2);
+        uint16_t* qd = reinterpret_cast<uint16_t*>(&qp[0][0]);   // [16][D / 2] pairs of int8
+        qd[(0 * G + wv) * (D / 2) + lane] = uint16_t((a0 & 255) | ((b0 & 255) << 8));
+        qd[(1 * G + wv) * (D / 2) + lane] = uint16_t((a1 & 255) | ((b1 & 255) << 8));
+        qd[(2 * G + wv) * (D / 2) + lane] = uint16_t((a2 & 255) | ((b2 & 255) << 8));
+        if (lane == 0) qe[wv] = e;
       }
     }
     __syncthreads();
     u32x4 qb[KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(&qp[kr][16 * ks + 4 * kg]);
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qb[ks] = MSB ? *reinterpret_cast<const u32x4*>(&qp[kr][16 * ks + 4 * kg])
+                   : *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(&qp[0][0]) + kr * D +
+                                                     64 * ks + 16 * kg);
+    const int ekr = MSI ? qe[kr < G ? kr : 0] : 0;
     for (int b = 0; wv + kWaves * b < ntile; b += UT) {
       if (b > 0) load_tiles(b);
 #pragma unroll
       for (int u = 0; u < UT; ++u) {
         const int tile = wv + kWaves * (b + u);   // wave-uniform
         if (tile < ntile) {
-          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int ks = 0; ks < KSTEPS; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kt[u][ks]),
-                                                          __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
-          // lane kr < G: column kr (rows 4 kg .. 4 kg + 3 of the tile) plus
+          // lane kr < G: column kr (rows 4 kg .. 4 kg + 3 of the tile) with
           // columns kr + G and kr + 2G (DPP row shifts left by G and 2G)
-          float4 sv;
-          sv.x = acc[0] + dpp_mov<0x100 + G>(acc[0]) + dpp_mov<0x100 + 2 * G>(acc[0]);
-          sv.y = acc[1] + dpp_mov<0x100 + G>(acc[1]) + dpp_mov<0x100 + 2 * G>(acc[1]);
-          sv.z = acc[2] + dpp_mov<0x100 + G>(acc[2]) + dpp_mov<0x100 + 2 * G>(acc[2]);
-          sv.w = acc[3] + dpp_mov<0x100 + G>(acc[3]) + dpp_mov<0x100 + 2 * G>(acc[3]);
-          // rows past the chunk score 0 and are never read; the index stays
-          // below kChunkMax (16 ceil(n / 16) <= kChunkMax)
-          if (kr < G) *reinterpret_cast<float4*>(&sc[kr][16 * tile + 4 * kg]) = sv;
+          float sv[4];
+          if constexpr (MSB) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kt[u][ks]),
+                                                            __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sv[i] = acc[i] + dpp_mov<0x100 + G>(acc[i]) + dpp_mov<0x100 + 2 * G>(acc[i]);
+          } else {
+            i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+              acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, kt[u][ks]),
+                                                          __builtin_bit_cast(i32x4, qb[ks]), acc, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sv[i] = digit_score(acc[i], dpp_mov_i<0x100 + G>(acc[i]), dpp_mov_i<0x100 + 2 * G>(acc[i]), ekr);
+          }
+          if (kr < G) {
+            float* dst = &sc[kr][16 * tile + 4 * kg];
+            if constexpr (MSB) {
+              // rows past the chunk score 0 and are never read; the index
+              // stays below kChunkMax (16 ceil(n / 16) <= kChunkMax)
+              *reinterpret_cast<float4*>(dst) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+            } else {
+              // int8: only the cache rows (row nrow may be the token's, scored by wave 0)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (16 * tile + 4 * kg + i < nrow) dst[i] = sv[i];
+            }
+          }
         }
       }
     }

@@ -36,6 +36,33 @@ __device__ __forceinline__ uint32_t q_part_bf16(float x, int p) {
   return f32_to_bf16(r - bf16_to_f32(mid));
 }
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// The int8 query operand of the matrix cores: a head's scaled query x is
+// taken as the integers X = rint(x 2^E), E chosen per head so that
+// max |x| 2^E lies in [2^21, 2^22) (query_exp_i8), and each X splits
+// exactly into three int8 digits, X = d0 + 2^8 d1 + 2^16 d2 with d0 and d1
+// in [-128, 127] and |d2| <= 65. Returns the digits as the low bytes of
+// an int each.
+__device__ __forceinline__ int query_exp_i8(float m) {   // m = max |x| over the head
+  return m > 0.0f ? 22 - __builtin_amdgcn_frexp_expf(m) : 0;
+}
+__device__ __forceinline__ void query_digits_i8(float x, int e, int& d0, int& d1, int& d2) {
+  const int X = int(rintf(ldexpf(x, e)));
+  d0 = ((X + 128) & 255) - 128;
+  const int X1 = (X - d0) >> 8;   // X - d0 is a multiple of 256
+  d1 = ((X1 + 128) & 255) - 128;
+  d2 = (X1 - d1) >> 8;
+}
+// S0 + 2^8 S1 + 2^16 S2 of a row's three digit sums, times 2^-e
+__device__ __forceinline__ float digit_score(int s0, int s1, int s2, int e) {
+  return ldexpf(fmaf(float(s2), 65536.0f, fmaf(float(s1), 256.0f, float(s0))), -e);
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+
 constexpr int kChunkMax = 256;  // cache positions per split
 constexpr int kSplitMax = 256;  // splits per kv head
 constexpr float kLog2e = 1.4426950408889634f;

@@ -99,8 +99,13 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
   const int sub = lane / LPR;
   const int li = lane % LPR;
   const int d0 = li * DPL;
-  constexpr bool MS = KVT == 1 && 3 * G <= 16 && D % 32 == 0;   // scores on the matrix cores
-  constexpr int KSTEPS = D / 32;        // matrix steps (ring slots) per 16-row tile
+  // scores on the matrix cores: bf16 caches (three bf16 parts of q) and
+  // int8 caches (three int8 digits of q, the batched kernel's scheme)
+  constexpr bool MSB = KVT == 1 && 3 * G <= 16 && D % 32 == 0;
+  constexpr bool MSI = KVT == 2 && 3 * G <= 16 && D == 128;
+  constexpr bool MS = MSB || MSI;
+  constexpr int KPS = MSI ? 64 : 32;    // dims per matrix step
+  constexpr int KSTEPS = D / KPS;       // matrix steps (ring slots) per 16-row tile
   static_assert(!MS || U % KSTEPS == 0, "whole tiles per ring");
   constexpr int QPAIRS = 16 * D / 2;    // B operand words
   constexpr int QPT = (QPAIRS + NW * 64 - 1) / (NW * 64);
@@ -133,18 +138,22 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + size_t(r) * RB));
   };
   // matrix-core key waves: slot k holds step k % KSTEPS of the wave's tile
-  // k / KSTEPS (chunk tile hw + 4 (k / KSTEPS)), row kr, dims 32 step + 8 kg
+  // k / KSTEPS (chunk tile hw + 4 (k / KSTEPS)), row kr, dims KPS step + KPS / 4 kg
   const uint8_t* ksrc = reinterpret_cast<const uint8_t*>(a.kc) + (size_t(j) * a.max_ctx + t0) * RB;
   auto kload = [&](int k) {
     int r = 16 * (hw + 4 * (k / KSTEPS)) + kr;
     r = r < nc ? r : rlast;
     return __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(ksrc + size_t(r) * RB + (32 * (k % KSTEPS) + 8 * kg) * 2));
+        reinterpret_cast<const u32x4*>(ksrc + size_t(r) * RB + (KPS * (k % KSTEPS) + KPS / 4 * kg) * S::EB));
   };
   // the B operand's words of this thread: q first, so waiting for it does
   // not wait for the ring
-  float2 qx[MS ? QPT : 1];
-  if constexpr (MS) {
+  float2 qx[MSB ? QPT : 1];
+  float2 qi = {0.0f, 0.0f};   // int8: wave wv < G holds dims 2 lane, 2 lane + 1 of head wv
+  if constexpr (MSI) {
+    if (wv < G) qi = *reinterpret_cast<const float2*>(a.q + (j * G + wv) * D + 2 * lane);
+  }
+  if constexpr (MSB) {
 #pragma unroll
     for (int r = 0; r < QPT; ++r) {
       const int e = tid + r * NW * 64;   // word e: column e / (D / 2), dims 2 (e % (D / 2)) + 0, 1
@@ -191,27 +200,48 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
   }
 
   uint32_t* qp = reinterpret_cast<uint32_t*>(ored);   // [16][D / 2] words; 16 D 2 <= NW G D 4 bytes
+  int* qe = role;   // int8: each head's exponent (G <= 4 words; the role word is set only at the combine)
   if constexpr (MS) {
     const float qscale = kLog2e / sqrtf(float(D));
+    if constexpr (MSB) {
 #pragma unroll
-    for (int r = 0; r < QPT; ++r) {
-      const int e = tid + r * NW * 64;
-      if (e < QPAIRS) {
-        const int p = (e / (D / 2)) / G;   // 3 and above: a zero column (its q words are zero)
-        qp[e] = q_part_bf16(qx[r].x * qscale, p) | (q_part_bf16(qx[r].y * qscale, p) << 16);
+      for (int r = 0; r < QPT; ++r) {
+        const int e = tid + r * NW * 64;
+        if (e < QPAIRS) {
+          const int p = (e / (D / 2)) / G;   // 3 and above: a zero column (its q words are zero)
+          qp[e] = q_part_bf16(qx[r].x * qscale, p) | (q_part_bf16(qx[r].y * qscale, p) << 16);
+        }
       }
+    } else if (wv < G) {
+      // int8: wave h < G builds head h's digit columns h, G + h, 2G + h
+      // (D bytes each; columns 3G and up are never read)
+      const float x0 = qi.x * qscale, x1 = qi.y * qscale;
+      const int e = query_exp_i8(wave_max(fmaxf(fabsf(x0), fabsf(x1))));
+      int a0, a1, a2, b0, b1, b2;
+      query_digits_i8(x0, e, a0, a1, a2);
+      query_digits_i8(x1, e, b0, b1, b2);
+      uint16_t* qd = reinterpret_cast<uint16_t*>(qp);   // [16][D / 2] pairs of int8
+      qd[(0 * G + wv) * (D / 2) + lane] = uint16_t((a0 & 255) | ((b0 & 255) << 8));
+      qd[(1 * G + wv) * (D / 2) + lane] = uint16_t((a1 & 255) | ((b1 & 255) << 8));
+      qd[(2 * G + wv) * (D / 2) + lane] = uint16_t((a2 & 255) | ((b2 & 255) << 8));
+      if (lane == 0) qe[wv] = e;
     }
     __syncthreads();
   }
 
-  if (MS && keys) {
+  if (keys) {
+  if constexpr (MS) {
     // ---- scores (log2 units) on the matrix cores, 16-row tiles
     u32x4 qb[KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(qp + kr * (D / 2) + 16 * ks + 4 * kg);
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qb[ks] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(qp) + kr * D * S::EB +
+                                               (KPS * ks + KPS / 4 * kg) * S::EB);
+    const int ekr = MSI ? qe[kr < G ? kr : 0] : 0;
     const int ntile = (nc + 15) / 16;
     const int nk = hw < ntile ? (ntile - hw + 3) / 4 * KSTEPS : 0;   // slots this wave consumes
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    i32x4 iacc = {0, 0, 0, 0};
     for (int k0 = 0; k0 < nk; k0 += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -219,24 +249,39 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
         ring[u] = kload(k0 + U + u);
         if (k0 + u < nk) {   // wave-uniform
           const int ks = u % KSTEPS;
-          if (ks == 0) acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
-                                                        __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
-          if (ks == KSTEPS - 1) {
+          float sv[4];
+          if constexpr (MSB) {
+            if (ks == 0) acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
+                                                          __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
             // lane kr < G: head kr's three columns (DPP row shifts left by G, 2G)
-            float4 sv;
-            sv.x = acc[0] + dpp_mov<0x100 + G>(acc[0]) + dpp_mov<0x100 + 2 * G>(acc[0]);
-            sv.y = acc[1] + dpp_mov<0x100 + G>(acc[1]) + dpp_mov<0x100 + 2 * G>(acc[1]);
-            sv.z = acc[2] + dpp_mov<0x100 + G>(acc[2]) + dpp_mov<0x100 + 2 * G>(acc[2]);
-            sv.w = acc[3] + dpp_mov<0x100 + G>(acc[3]) + dpp_mov<0x100 + 2 * G>(acc[3]);
-            // rows 16 tile + 4 kg .. + 3 (past nc: never read); 16 ceil(nc / 16) <= cpad
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[i] = acc[i] + dpp_mov<0x100 + G>(acc[i]) + dpp_mov<0x100 + 2 * G>(acc[i]);
+          } else {
+            if (ks == 0) iacc = i32x4{0, 0, 0, 0};
+            iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, w),
+                                                         __builtin_bit_cast(i32x4, qb[ks]), iacc, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sv[i] = digit_score(iacc[i], dpp_mov_i<0x100 + G>(iacc[i]), dpp_mov_i<0x100 + 2 * G>(iacc[i]), ekr);
+          }
+          if (ks == KSTEPS - 1 && kr < G) {
             const int tile = hw + 4 * ((k0 + u) / KSTEPS);
-            if (kr < G) *reinterpret_cast<float4*>(sc + kr * cpad + 16 * tile + 4 * kg) = sv;
+            float* dst = sc + kr * cpad + 16 * tile + 4 * kg;
+            if constexpr (MSB) {
+              // rows 16 tile + 4 kg .. + 3 (past nc: never read); 16 ceil(nc / 16) <= cpad
+              *reinterpret_cast<float4*>(dst) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+            } else {
+              // int8: only the streamed rows (row nc may be the token's, scored by wave 0)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (16 * tile + 4 * kg + i < nc) dst[i] = sv[i];
+            }
           }
         }
       }
     }
-  } else if (keys) {
+  } else {
     const float qscale = kLog2e / sqrtf(float(D));
     float qv[G][DPL];
 #pragma unroll
@@ -268,6 +313,7 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
         }
       }
     }
+  }
     if constexpr (I8) {
 #pragma unroll
       for (int k = 0; k < NSC; ++k) {
