@@ -322,6 +322,43 @@ def test_attn_i8_cache_appends_and_matches_oracle(gpu, nq, nkv, max_ctx, positio
     assert st.check_err() == 0
 
 
+@pytest.mark.parametrize("kernel", ["DEC_ATTN_BATCHED", "DEC_ATTN_STREAM"])
+@pytest.mark.parametrize("nq,nkv", [(32, 8), (16, 8), (8, 8)])
+def test_attn_i8_matrix_core_scores_keep_22_bits_of_the_query(gpu, kernel, nq, nkv):
+    """int8 caches with up to four query heads per kv head score on the
+    matrix cores with each scaled query head as integers of 22 bits (three
+    int8 digits). With queries eight times larger than usual (a sharp
+    softmax), these inputs land within 1.4e-6 relative L2 of the oracle when
+    computed in float32 with a 22-bit query and at least 1.1e-4 away with a
+    14-bit one (two digits; measured on the CPU): the bound is 1e-5."""
+    d, max_ctx = 128, 1000
+    cfg = synth.tiny(hidden=256, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, ffn=256, wtype="bf16",
+                     ntype="bf16", kvtype="i8", ctx=0, steps=max_ctx, seed=13)
+    st = DecodeStack(cfg, n_layers=1, flags=getattr(L, kernel))
+    std = 0.02 * np.sqrt(4096)
+    pre = synth.rand_cache((13, 1, max_ctx), nkv, max_ctx, d, "i8", std)
+    prv = synth.rand_cache((13, 2, max_ctx), nkv, max_ctx, d, "i8", std)
+    st.set_prefill(0, pre, prv)
+    codes_k, sc_k = pre.data.copy(), pre.scales.copy()
+    codes_v, sc_v = prv.data.copy(), prv.scales.copy()
+    for i, p in enumerate((999, 500)):
+        q = synth.rand_f32((13, 3, i), (nq, d), std=8 * std)
+        kn = synth.rand_f32((13, 4, i), (nkv, d), std=std)
+        vn = synth.rand_f32((13, 5, i), (nkv, d), std=std)
+        st.q.copy_(torch.from_numpy(q.reshape(-1)))
+        st.Kstage[0].copy_(torch.from_numpy(kn))
+        st.Vstage[0].copy_(torch.from_numpy(vn))
+        st.set_pos(p)
+        L.dec_attn_splitk(st.desc, st.state[0])
+        torch.cuda.synchronize()
+        (codes_k[:, p], sc_k[:, p]), (codes_v[:, p], sc_v[:, p]) = oracle.quantize_i8(kn), oracle.quantize_i8(vn)
+        Kd = oracle.ref.cache_values(codes_k[:, : p + 1], "i8", np.float64, sc_k[:, : p + 1])
+        Vd = oracle.ref.cache_values(codes_v[:, : p + 1], "i8", np.float64, sc_v[:, : p + 1])
+        ref = oracle.attend(q.astype(np.float64), Kd, Vd, nq // nkv)
+        assert rel_l2(st.attn.cpu().numpy(), ref.reshape(-1)) <= TOL, f"{kernel} pos {p}"
+    assert st.check_err() == 0
+
+
 def test_combiner_give_up_sets_sync_error_and_recovers(gpu):
     """The attention combine's failure path, forced from the host:
     DEC_TEST_NO_WAIT makes every combiner but the last arrival of a kv head
