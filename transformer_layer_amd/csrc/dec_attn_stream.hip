@@ -230,90 +230,94 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
   }
 
   if (keys) {
-  if constexpr (MS) {
-    // ---- scores (log2 units) on the matrix cores, 16-row tiles
-    u32x4 qb[KSTEPS];
+    if constexpr (MS) {
+      // ---- scores (log2 units) on the matrix cores, 16-row tiles
+      u32x4 qb[KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      qb[ks] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(qp) + kr * D * S::EB +
-                                               (KPS * ks + KPS / 4 * kg) * S::EB);
-    const int ekr = MSI ? qe[kr < G ? kr : 0] : 0;
-    const int ntile = (nc + 15) / 16;
-    const int nk = hw < ntile ? (ntile - hw + 3) / 4 * KSTEPS : 0;   // slots this wave consumes
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    i32x4 iacc = {0, 0, 0, 0};
-    for (int k0 = 0; k0 < nk; k0 += U) {
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        qb[ks] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(qp) + kr * D * S::EB +
+                                                 (KPS * ks + KPS / 4 * kg) * S::EB);
+      const int ekr = MSI ? qe[kr < G ? kr : 0] : 0;
+      const int ntile = (nc + 15) / 16;
+      const int nk = hw < ntile ? (ntile - hw + 3) / 4 * KSTEPS : 0;   // slots this wave consumes
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      i32x4 iacc = {0, 0, 0, 0};
+      for (int k0 = 0; k0 < nk; k0 += U) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const u32x4 w = ring[u];
-        ring[u] = kload(k0 + U + u);
-        if (k0 + u < nk) {   // wave-uniform
-          const int ks = u % KSTEPS;
-          float sv[4];
-          if constexpr (MSB) {
-            if (ks == 0) acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
-                                                          __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
-            // lane kr < G: head kr's three columns (DPP row shifts left by G, 2G)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sv[i] = acc[i] + dpp_mov<0x100 + G>(acc[i]) + dpp_mov<0x100 + 2 * G>(acc[i]);
-          } else {
-            if (ks == 0) iacc = i32x4{0, 0, 0, 0};
-            iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, w),
-                                                         __builtin_bit_cast(i32x4, qb[ks]), iacc, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sv[i] = digit_score(iacc[i], dpp_mov_i<0x100 + G>(iacc[i]), dpp_mov_i<0x100 + 2 * G>(iacc[i]), ekr);
-          }
-          if (ks == KSTEPS - 1 && kr < G) {
-            const int tile = hw + 4 * ((k0 + u) / KSTEPS);
-            float* dst = sc + kr * cpad + 16 * tile + 4 * kg;
+        for (int u = 0; u < U; ++u) {
+          const u32x4 w = ring[u];
+          ring[u] = kload(k0 + U + u);
+          if (k0 + u < nk) {   // wave-uniform
+            const int ks = u % KSTEPS;   // a constant once unrolled
             if constexpr (MSB) {
-              // rows 16 tile + 4 kg .. + 3 (past nc: never read); 16 ceil(nc / 16) <= cpad
-              *reinterpret_cast<float4*>(dst) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+              if (ks == 0) acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
+                                                            __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
             } else {
-              // int8: only the streamed rows (row nc may be the token's, scored by wave 0)
+              if (ks == 0) iacc = i32x4{0, 0, 0, 0};
+              iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, w),
+                                                           __builtin_bit_cast(i32x4, qb[ks]), iacc, 0, 0, 0);
+            }
+            if (ks == KSTEPS - 1) {
+              // lane kr < G: head kr's three columns (DPP row shifts left by G, 2G)
+              float sv[4];
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (16 * tile + 4 * kg + i < nc) dst[i] = sv[i];
+              for (int i = 0; i < 4; ++i) {
+                if constexpr (MSB)
+                  sv[i] = acc[i] + dpp_mov<0x100 + G>(acc[i]) + dpp_mov<0x100 + 2 * G>(acc[i]);
+                else
+                  sv[i] = digit_score(iacc[i], dpp_mov_i<0x100 + G>(iacc[i]), dpp_mov_i<0x100 + 2 * G>(iacc[i]), ekr);
+              }
+              const int tile = hw + 4 * ((k0 + u) / KSTEPS);
+              float* dst = sc + kr * cpad + 16 * tile + 4 * kg;
+              if (kr < G) {
+                if constexpr (MSB) {
+                  // rows 16 tile + 4 kg .. + 3 (past nc: never read); 16 ceil(nc / 16) <= cpad
+                  *reinterpret_cast<float4*>(dst) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+                } else {
+                  // int8: only the streamed rows (row nc may be the token's, scored by wave 0)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i)
+                    if (16 * tile + 4 * kg + i < nc) dst[i] = sv[i];
+                }
+              }
+            }
+          }
+        }
+      }
+    } else {
+      const float qscale = kLog2e / sqrtf(float(D));
+      float qv[G][DPL];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < DPL; e += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(a.q + (j * G + hh) * D + d0 + e);
+          qv[hh][e] = x.x * qscale; qv[hh][e + 1] = x.y * qscale;
+          qv[hh][e + 2] = x.z * qscale; qv[hh][e + 3] = x.w * qscale;
+        }
+      // ---- scores (log2 units): s_t = (q . k_t) log2(e) / sqrt(d)
+      for (int k0 = 0; k0 < nsteps; k0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const u32x4 w = ring[u];
+          ring[u] = load(k0 + U + u);
+          if (k0 + u < nsteps) {
+            const int t = row_of(k0 + u);
+            float kf[DPL];
+            unpack_row<KVT>(w, kf);
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+              float p = 0.0f;
+#pragma unroll
+              for (int e = 0; e < DPL; ++e) p = fmaf(qv[hh][e], kf[e], p);
+              p = group_sum<LPR>(p);
+              if (t < nc && li == 0) sc[hh * cpad + t] = p;
             }
           }
         }
       }
     }
-  } else {
-    const float qscale = kLog2e / sqrtf(float(D));
-    float qv[G][DPL];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < DPL; e += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(a.q + (j * G + hh) * D + d0 + e);
-        qv[hh][e] = x.x * qscale; qv[hh][e + 1] = x.y * qscale;
-        qv[hh][e + 2] = x.z * qscale; qv[hh][e + 3] = x.w * qscale;
-      }
-    // ---- scores (log2 units): s_t = (q . k_t) log2(e) / sqrt(d)
-    for (int k0 = 0; k0 < nsteps; k0 += U) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const u32x4 w = ring[u];
-        ring[u] = load(k0 + U + u);
-        if (k0 + u < nsteps) {
-          const int t = row_of(k0 + u);
-          float kf[DPL];
-          unpack_row<KVT>(w, kf);
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) {
-            float p = 0.0f;
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) p = fmaf(qv[hh][e], kf[e], p);
-            p = group_sum<LPR>(p);
-            if (t < nc && li == 0) sc[hh * cpad + t] = p;
-          }
-        }
-      }
-    }
-  }
     if constexpr (I8) {
 #pragma unroll
       for (int k = 0; k < NSC; ++k) {
