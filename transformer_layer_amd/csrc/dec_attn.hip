@@ -35,7 +35,11 @@
 // score is the float32 dot product up to the order of its additions; two DPP
 // adds sum the three columns of a head. On the vector ALUs each 16 rows cost
 // about 250 instructions a wave (unpacking, products, lane folds), here 4
-// matrix operations and about 10 instructions.
+// matrix operations and about 10 instructions. An int8 cache does the same
+// with v_mfma_i32_16x16x64_i8: the codes as stored, and each query head as
+// 22-bit integers in three int8 digits (query_digits_i8), whose exact
+// integer sums combine in float32 and scale by 2^-E; its tile stores leave
+// out the token's own row, which wave 0 scores.
 //
 // Partials, arrival and combine: attn_finish (dec_attn_common.h).
 #include "dec_attn_common.h"
