@@ -359,6 +359,48 @@ def test_attn_i8_matrix_core_scores_keep_22_bits_of_the_query(gpu, kernel, nq, n
     assert st.check_err() == 0
 
 
+@pytest.mark.parametrize("kernel", ["DEC_ATTN_BATCHED", "DEC_ATTN_STREAM"])
+@pytest.mark.parametrize("kvtype", ["bf16", "i8"])
+def test_attn_matrix_core_scores_keep_a_nan_query_visible(gpu, kernel, kvtype):
+    """A NaN in one query head makes that head's output NaN, as float
+    arithmetic would (the int8 digits of a non-finite query poison the
+    head's scores instead of rounding it to an integer); the other heads of
+    the same kv head still match the oracle."""
+    d, nq, nkv, max_ctx, p = 128, 16, 4, 300, 299
+    cfg = synth.tiny(hidden=256, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, ffn=256, wtype="bf16",
+                     ntype="bf16", kvtype=kvtype, ctx=0, steps=max_ctx, seed=14)
+    st = DecodeStack(cfg, n_layers=1, flags=getattr(L, kernel))
+    std = 0.02 * np.sqrt(4096)
+    K = synth.rand_cache((14, 1, max_ctx), nkv, max_ctx, d, kvtype, std)
+    V = synth.rand_cache((14, 2, max_ctx), nkv, max_ctx, d, kvtype, std)
+    st.set_prefill(0, K, V)
+    sk = sv = None
+    if kvtype == "i8":
+        kn = synth.rand_f32((14, 4, 0), (nkv, d), std=std)
+        vn = synth.rand_f32((14, 5, 0), (nkv, d), std=std)
+        st.Kstage[0].copy_(torch.from_numpy(kn))
+        st.Vstage[0].copy_(torch.from_numpy(vn))
+        K.data[:, p], K.scales[:, p] = oracle.quantize_i8(kn)
+        V.data[:, p], V.scales[:, p] = oracle.quantize_i8(vn)
+        sk, sv = K.scales, V.scales
+    q = synth.rand_f32((14, 3, 0), (nq, d), std=std)
+    bad = 5                      # query head 5: kv head 1, second head of its group
+    q[bad, 17] = np.nan
+    st.q.copy_(torch.from_numpy(q.reshape(-1)))
+    st.set_pos(p)
+    L.dec_attn_splitk(st.desc, st.state[0])
+    torch.cuda.synchronize()
+    got = st.attn.cpu().numpy().reshape(nq, d)
+    assert np.isnan(got[bad]).all(), "the NaN query head's output"
+    Kd = oracle.ref.cache_values(K.data[:, : p + 1], kvtype, np.float64, None if sk is None else sk[:, : p + 1])
+    Vd = oracle.ref.cache_values(V.data[:, : p + 1], kvtype, np.float64, None if sv is None else sv[:, : p + 1])
+    q[bad] = 0.0
+    ref = oracle.attend(q.astype(np.float64), Kd, Vd, nq // nkv)
+    keep = [h for h in range(nq) if h != bad]
+    assert rel_l2(got[keep].reshape(-1), ref[keep].reshape(-1)) <= TOL
+    assert st.check_err() == 0
+
+
 def test_combiner_give_up_sets_sync_error_and_recovers(gpu):
     """The attention combine's failure path, forced from the host:
     DEC_TEST_NO_WAIT makes every combiner but the last arrival of a kv head

@@ -48,15 +48,24 @@ __device__ __forceinline__ int query_exp_i8(float m) {   // m = max |x| over the
   return m > 0.0f ? 22 - __builtin_amdgcn_frexp_expf(m) : 0;
 }
 __device__ __forceinline__ void query_digits_i8(float x, int e, int& d0, int& d1, int& d2) {
-  const int X = int(rintf(ldexpf(x, e)));
+  const float y = rintf(ldexpf(x, e));
+  const int X = fabsf(y) <= 4194304.0f ? int(y) : 0;   // 2^22; a non-finite x (poisoned head) gives 0
   d0 = ((X + 128) & 255) - 128;
   const int X1 = (X - d0) >> 8;   // X - d0 is a multiple of 256
   d1 = ((X1 + 128) & 255) - 128;
   d2 = (X1 - d1) >> 8;
 }
+// A head whose query holds a NaN or an infinity gets exponent
+// kQueryPoison instead: its scores are NaN, as the float arithmetic would
+// make them, rather than whatever the digits of a non-finite value give.
+constexpr int kQueryPoison = -1000000;
+__device__ __forceinline__ int query_exp_i8_checked(float m, bool finite) {
+  return finite ? query_exp_i8(m) : kQueryPoison;
+}
 // S0 + 2^8 S1 + 2^16 S2 of a row's three digit sums, times 2^-e
 __device__ __forceinline__ float digit_score(int s0, int s1, int s2, int e) {
-  return ldexpf(fmaf(float(s2), 65536.0f, fmaf(float(s1), 256.0f, float(s0))), -e);
+  const float v = ldexpf(fmaf(float(s2), 65536.0f, fmaf(float(s1), 256.0f, float(s0))), -e);
+  return e == kQueryPoison ? __builtin_nanf("") : v;
 }
 template <int CTRL>
 __device__ __forceinline__ int dpp_mov_i(int v) {

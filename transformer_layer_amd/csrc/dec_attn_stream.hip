@@ -216,7 +216,8 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
       // int8: wave h < G builds head h's digit columns h, G + h, 2G + h
       // (D bytes each; columns 3G and up are never read)
       const float x0 = qi.x * qscale, x1 = qi.y * qscale;
-      const int e = query_exp_i8(wave_max(fmaxf(fabsf(x0), fabsf(x1))));
+      const bool finite = __all(fabsf(x0) <= 3.4028235e38f && fabsf(x1) <= 3.4028235e38f);
+      const int e = query_exp_i8_checked(wave_max(fmaxf(fabsf(x0), fabsf(x1))), finite);
       int a0, a1, a2, b0, b1, b2;
       query_digits_i8(x0, e, a0, a1, a2);
       query_digits_i8(x1, e, b0, b1, b2);
