@@ -130,7 +130,9 @@ struct AttnShared {
 // Split s of kv head j (of ns live splits): store its partials from LDS,
 // then (unless the output projection combines) arrive and, for the last
 // arrivals, combine. Every thread of the workgroup calls it.
-template <int D, int G, int NW>
+// OW: how many per-wave copies of the output sums ored holds (their sum is
+// the split's o); NW unless the waves wrote disjoint dims into copy 0.
+template <int D, int G, int NW, int OW = NW>
 __device__ __forceinline__ void attn_finish(const AttnArgs& a, int j, int s, int ns, AttnShared sh) {
   // ---- this split's partials: o [j][s][G][D] and (m, l) [j][s][G][2], as
   // agent-scope 64-bit atomic stores (pairs of floats)
@@ -144,7 +146,7 @@ __device__ __forceinline__ void attn_finish(const AttnArgs& a, int j, int s, int
     const int hh = idx / D, dd = idx % D;
     float r = sh.ored[hh * D + dd];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r += sh.ored[(w * G + hh) * D + dd];
+    for (int w = 1; w < OW; ++w) r += sh.ored[(w * G + hh) * D + dd];
     return r;
   };
   for (int i2 = threadIdx.x; i2 < G * D / 2; i2 += kBlock) store_pair_agent(po + 2 * i2, osum(2 * i2), osum(2 * i2 + 1));

@@ -33,12 +33,17 @@
 // lane l reads row l % 16), its ring slots holding the tiles' 16-byte steps.
 // The B operand (three bf16 parts of each scaled query head) is built by all
 // eight waves, before any row arrives, in the per-wave output sums' LDS,
-// which stays unused until the sum of p * v.
+// which stays unused until the sum of p * v. The sum of p * v runs on the
+// matrix cores as well: the value waves store their rows transposed in
+// blocks of eight (the A operand layout, dims as its rows), the softmax
+// pass stores p as three bf16 parts (the B operand), and wave w sums dims
+// 16 w .. 16 w + 15 over every row, so no fold across waves is needed.
 //
 // LDS layout (bytes), rows padded to cpad (a whole number of eight-wave
 // row steps): [values cpad x row][scores G x cpad f32][per-wave output sums
 // NW x G x D f32][combine scratch][(m, l) G x 2 f32][role][int8: key and
-// value scales 2 x cpad f32].
+// value scales 2 x cpad f32][bf16 on the matrix cores: p parts 16 x cpad
+// bf16, 16-byte aligned].
 #include "dec_attn_common.h"
 
 namespace dec {
@@ -59,9 +64,14 @@ constexpr int kRing = 8;   // loads in flight per lane
 __host__ __device__ constexpr int stream_comb_bytes(int G) {
   return ((kSplitMax * G + G) * 4 + 15) / 16 * 16 + kLdsWaves * 64 * 16;
 }
-__host__ __device__ constexpr int stream_lds_bytes(int cpad, int rb, int G, int D, bool i8) {
+// bf16 caches with at most four query heads per kv head: scores and the sum
+// of p v on the matrix cores (the latter reads p as three bf16 parts)
+__host__ __device__ constexpr bool stream_matrix_cores(int kvtype, int G, int D) {
+  return kvtype == 1 && 3 * G <= 16 && D % 32 == 0;
+}
+__host__ __device__ constexpr int stream_lds_bytes(int cpad, int rb, int G, int D, bool i8, bool pvm) {
   return cpad * rb + G * cpad * 4 + kLdsWaves * G * D * 4 + stream_comb_bytes(G) + G * 2 * 4 + 16 +
-         (i8 ? 2 * cpad * 4 : 0);
+         (i8 ? 2 * cpad * 4 : 0) + (pvm ? 16 * cpad * 2 + 16 : 0);
 }
 
 template <int D, int KVT, int G>
@@ -101,7 +111,7 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
   const int d0 = li * DPL;
   // scores on the matrix cores: bf16 caches (three bf16 parts of q) and
   // int8 caches (three int8 digits of q, the batched kernel's scheme)
-  constexpr bool MSB = KVT == 1 && 3 * G <= 16 && D % 32 == 0;
+  constexpr bool MSB = stream_matrix_cores(KVT, G, D);
   constexpr bool MSI = KVT == 2 && 3 * G <= 16 && D == 128;
   constexpr bool MS = MSB || MSI;
   constexpr int KPS = MSI ? 64 : 32;    // dims per matrix step
@@ -122,6 +132,9 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
   int* role = reinterpret_cast<int*>(stat + G * 2);
   float* ksl = reinterpret_cast<float*>(role + 4);                        // int8: [cpad] key scales
   float* vsl = ksl + cpad;                                                // int8: [cpad] value scales
+  // bf16, matrix cores: p as three bf16 parts, [16][cpad] (column part G + head)
+  uint16_t* pp = reinterpret_cast<uint16_t*>(
+      smem + (int(reinterpret_cast<uint8_t*>(I8 ? vsl + cpad : ksl) - smem) + 15) / 16 * 16);
 
   // waves 0-3 stream keys, waves 4-7 values: row r of the chunk is read by
   // wave (r / RPW) % 4 of its half at step r / RPH
@@ -358,7 +371,10 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
       }
     }
   } else {
-    // ---- values into LDS as they arrive
+    // ---- values into LDS as they arrive. For the matrix cores the rows go
+    // in blocks of eight, transposed: dim d of rows 8 b .. 8 b + 7 is the 16
+    // bytes at block b, position pi(d) = (d % 8) (D / 8) + d / 8 (so the 16
+    // lanes of a row write 16 consecutive positions of a block)
     for (int k0 = 0; k0 < nsteps; k0 += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -366,9 +382,22 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
         ring[u] = load(k0 + U + u);
         if (k0 + u < nsteps) {
           const int t = row_of(k0 + u);   // < cpad: the steps cover at most cpad rows
-          if (!I8 || t < nc) *reinterpret_cast<u32x4*>(vbuf + t * RB + li * 16) = w;   // int8: row nc is the token's
+          if constexpr (MSB) {
+            uint16_t* vt = reinterpret_cast<uint16_t*>(vbuf) + ((t / 8) * D + li) * 8 + t % 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vt[e * (D / 8) * 8] = uint16_t(w[e / 2] >> (16 * (e % 2)));
+          } else if (!I8 || t < nc) {
+            *reinterpret_cast<u32x4*>(vbuf + t * RB + li * 16) = w;   // int8: row nc is the token's
+          }
         }
       }
+    }
+    if constexpr (MSB) {
+      // rows past the streamed steps up to a whole 32-row matrix step: zero
+      // (their p is zero too; uninitialized LDS could hold NaN bits)
+      const int z0 = nsteps * RPH, z1 = (n + 31) / 32 * 32;
+      for (int i = hw * kWave + lane; i < (z1 - z0) / 8 * D; i += 4 * kWave)
+        *reinterpret_cast<u32x4*>(vbuf + ((z0 / 8) * D + i) * 16) = u32x4{0u, 0u, 0u, 0u};
     }
   }
   __syncthreads();
@@ -383,12 +412,52 @@ __global__ __launch_bounds__(kLdsWaves * 64) void attn_stream_kernel(AttnArgs a)
     for (int i = lane; i < n; i += kWave) {
       const float p = exp2f((I8 ? sc[hh * cpad + i] * ksl[i] : sc[hh * cpad + i]) - m);
       sc[hh * cpad + i] = I8 ? p * vsl[i] : p;
+      if constexpr (MSB) {
+#pragma unroll
+        for (int pt = 0; pt < 3; ++pt) pp[(pt * G + hh) * cpad + i] = uint16_t(q_part_bf16(p, pt));
+      }
       l += p;
+    }
+    if constexpr (MSB) {
+      for (int i = n + lane; i < (n + 31) / 32 * 32; i += kWave)
+#pragma unroll
+        for (int pt = 0; pt < 3; ++pt) pp[(pt * G + hh) * cpad + i] = 0;
     }
     l = wave_sum(l);
     if (lane == 0) { stat[hh * 2] = m; stat[hh * 2 + 1] = l; }
   }
   __syncthreads();
+
+  if constexpr (MSB) {
+    // ---- o = sum_t p_t v_t on the matrix cores: wave w takes dims 16 w ..
+    // 16 w + 15 (A operand: lane l holds dim 16 w + l % 16 of rows 32 ks +
+    // 8 (l / 16) .. + 7, one block of the transposed values) over every row;
+    // B holds p's three bf16 parts of each head (column part G + head), so
+    // a head's three columns sum to the float32 p times exact bf16 values
+    constexpr int NT = D / 16;
+    if (wv < NT) {
+      const int m = 16 * wv + kr;
+      const int dp = (m % 8) * (D / 8) + m / 8;
+      const int c = kr < 3 * G ? kr : 0;   // columns 3G and up repeat column 0 (never read)
+      const int nks = (n + 31) / 32;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int ks = 0; ks < nks; ++ks) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(vbuf + ((4 * ks + kg) * D + dp) * 16);
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(pp + c * cpad + 32 * ks + 8 * kg);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                      __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+      }
+      // lane kr < G: head kr, dims 16 w + 4 kg .. + 3 (every lane takes part in the shifts)
+      float ov[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = acc[i] + dpp_mov<0x100 + G>(acc[i]) + dpp_mov<0x100 + 2 * G>(acc[i]);
+      if (kr < G)
+        *reinterpret_cast<float4*>(ored + kr * D + 16 * wv + 4 * kg) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+    }
+    __syncthreads();
+    attn_finish<D, G, NW, 1>(a, j, s, ns, AttnShared{ored, stat, wts, den, accs, role});
+    return;
+  }
 
   // ---- o = sum_t p_t v_t, all eight waves over the LDS values. int8 and
   // bf16 rows are read eight bytes a lane (8 codes, 4 bf16 dims), so the rows
@@ -462,7 +531,8 @@ static bool stream_fits(int n_q, int n_kv, int head_dim, int kvtype, int chunk) 
   int rps, rb;
   stream_row_shape(head_dim, kvtype, &rps, &rb);
   const int cpad = (chunk + rps - 1) / rps * rps;
-  return stream_lds_bytes(cpad, rb, n_q / n_kv, head_dim, kvtype == 2) <= kLdsBudget;
+  return stream_lds_bytes(cpad, rb, n_q / n_kv, head_dim, kvtype == 2,
+                          stream_matrix_cores(kvtype, n_q / n_kv, head_dim)) <= kLdsBudget;
 }
 
 int attn_lds_max_chunk(int n_q, int n_kv, int head_dim, int kvtype) {
@@ -481,7 +551,7 @@ static hipError_t go_attn_stream(const AttnArgs& a, hipStream_t s) {
   using S = StreamShape<D, KVT>;
   const int g = a.nq / a.nkv;
   const int cpad = (a.chunk + S::RPS - 1) / S::RPS * S::RPS;
-  const int lds = stream_lds_bytes(cpad, S::RB, g, D, KVT == 2);
+  const int lds = stream_lds_bytes(cpad, S::RB, g, D, KVT == 2, stream_matrix_cores(KVT, g, D));
   if (lds > kLdsBudget) return hipErrorInvalidValue;
   const dim3 grid(a.nkv * a.nsplit), block(kLdsWaves * 64);
   switch (g) {
