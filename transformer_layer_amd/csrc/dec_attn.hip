@@ -518,6 +518,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 }
 
 // splits per kv head for about one workgroup per compute unit (at most 64)
+constexpr int kLongChunkGroups = 512;   // two workgroups per compute unit of the 256
+
 static int target_splits(int n_kv) {
   int splits = kLdsTargetGroups / n_kv;
   return splits < 1 ? 1 : splits > 64 ? 64 : splits;
@@ -533,11 +535,18 @@ static int batched_default_chunk(int n_kv, int head_dim, int kvtype, int max_ctx
   int c = (max_ctx + splits - 1) / splits;
   c = ((c + 15) / 16) * 16;
   if (c > one_batch) c = one_batch;
-  // bf16 head_dim 128: at most 96 rows, three quarters of a batch (more
-  // splits, shorter chains per workgroup; measured against 128: 9B-shaped
-  // layer at 8320 positions 16.6 -> 16.0 us, 7B-shaped at 2112 positions
-  // 12.3 -> 11.95 us)
-  if (head_dim == 128 && kvtype == 1 && c > 96) c = 96;
+  // bf16 and int8 heads of 128 (scores on the matrix cores): 256-row chunks
+  // once they still give two workgroups per compute unit, else at most 96
+  // rows (more splits, shorter chains per workgroup). Measured, 9B-shaped
+  // stacks: 4-bit at 16640 positions 437.8 -> 448.5 tok/s with 256 rows
+  // (520 workgroups), at 33024 332.1 -> 360.4 (1032), bf16 at 16640 274.6 ->
+  // 279.4 and at 33024 229.4 -> 241.8; at 12544 positions (392 workgroups)
+  // 256 rows lost (469.9 -> 464.2, 287.2 -> 285.2), and 96 rows beat 256 on
+  // the int8 cache at 8448 (496.1 -> 499.1)
+  if (head_dim == 128 && (kvtype == 1 || kvtype == 2)) {
+    if (n_kv * ((max_ctx + kChunkMax - 1) / kChunkMax) >= kLongChunkGroups) return kChunkMax;
+    if (c > 96) c = 96;
+  }
   return c;
 }
 
