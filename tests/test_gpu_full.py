@@ -4,6 +4,8 @@ benchmark times (the same kernels, grids and split counts).
 * The first two layers of each 1B/7B/9B-shaped workload, at its real cache
   length, for three decode steps: every layer's output against the oracle
   run independently, and the cache slots the GPU wrote.
+* The first two layers of the 9B-shaped stacks over a 16384-position cache
+  (the long-cache attention plan: 256-row chunks, 65 splits a kv head).
 * One decode token through every layer of the 1B-, 7B-, 9B-shaped bf16 and
   the 9B-shaped 4-bit stacks, layer by layer.
 * The five fused kernels against the ten per-op kernels at the 9B shapes
@@ -94,6 +96,43 @@ def test_first_layers_at_full_shape(gpu, name):
             check_rounded_slot(K[l, :, p], ora.K[l][:, p], k_ex, "bf16", TOL)
             check_rounded_slot(V[l, :, p], ora.V[l][:, p], v_ex, "bf16", TOL)
         assert np.all(K[l, :, cfg.ctx + nsteps:] == 0x7FC1) and np.all(V[l, :, cfg.ctx + nsteps:] == 0x7FC1)
+    _release()
+
+
+@pytest.mark.parametrize("name", ["C4", "C5"])
+def test_first_layers_over_a_long_cache(gpu, name):
+    """The long-cache plan: at 16384 cached positions the batched attention
+    kernel takes 256-row chunks (65 splits per kv head, 520 workgroups; its
+    key tiles and value rows arrive in several batches, and it combines the
+    splits itself). The first two layers of the 9B-shaped stacks, two decode
+    steps, every layer's output against the oracle."""
+    cfg = synth.CONFIGS[name].with_(ctx=16384)
+    nl, nsteps = 2, 2
+    ora = oracle.Oracle.from_config(cfg, n_layers=nl, with_globals=False)
+    st = DecodeStack(cfg, n_layers=nl)
+    per_split = cfg.n_q_heads * (cfg.head_dim + 2)
+    assert L.dec_attn_part_floats(st.desc) == 65 * per_split, "not the 256-row plan"
+    for l in range(nl):
+        st.set_layer(l, ora.layers[l])
+        st.set_prefill(l, *synth.prefill(cfg, l))
+    embed = synth.embedding(cfg)
+    st.set_embedding(embed)
+    ora.glob = {"embed": embed}
+    toks = synth.tokens(cfg)
+    rec = torch.zeros(nl + 1, cfg.hidden, dtype=torch.float32, device="cuda")
+    worst = 0.0
+    for i in range(nsteps):
+        p = cfg.ctx + i
+        st.set_pos(p)
+        st.set_token(int(toks[i]))
+        st.token_step(record=rec)
+        got = rec.cpu().numpy()
+        ref = ora.step(int(toks[i]), p)
+        for l in range(1, nl + 1):
+            worst = max(worst, rel_l2(got[l], ref[l]))
+    print(f"{name} at {cfg.ctx} positions: worst layer relative L2 {worst:.2e}")
+    assert st.check_err() == 0
+    assert worst <= TOL, f"{name}: worst layer-output relative L2 {worst:.3e}"
     _release()
 
 

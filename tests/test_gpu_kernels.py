@@ -206,6 +206,7 @@ KERNEL_CASES = [
     (128, 32, 8, 4352, (4351,), 0),
     (128, 16, 4, 300, (0, 1, 16, 17, 299), 16),   # four-head groups (matrix-core scores), one-row splits
     (64, 4, 2, 333, (332, 5, 32), 33),             # two-head groups, 16-row tiles ending inside a chunk
+    (128, 32, 8, 1100, (1099, 600), 256),          # 256-row chunks (the long-cache plan): several load batches
 ]
 
 
@@ -273,6 +274,7 @@ I8_CASES = [
     (16, 2, 700, (699, 350, 48), 48),     # the token alone in its split at 48
     (16, 2, 2200, (2199,), 100),
     (32, 4, 4200, (4100, 4101), 0),
+    (32, 8, 1100, (1099, 513), 256),     # 256-row chunks
 ]
 
 
